@@ -1,0 +1,24 @@
+"""CPU oracle (fp64, numpy) for varlen attention and the AttentionUpdate merge.
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, by the smoke check and by the
+benchmark's CPU-baseline leg, never by the product library. It shares no
+code with the HIP kernels or their host launcher.
+
+Parity status per function (what pins it; see tests/test_oracle_*.py):
+  varlen_attention / varlen_attention_rows -- pinned: brute force with
+      math.fsum on tiny cases, torch CPU fp64 scaled_dot_product_attention on
+      padded per-sequence inputs, closed forms (Q = 0, causal row 0, constant
+      V, single key) and invariants (packing, GQA = MHA on repeated K/V,
+      key shift, scale folding, lse bounds, sequence permutation).
+  attn_update -- pinned: hand-worked golden values, chunked + merged equals
+      unchunked attention, sp = 1 identity, chunk permutation, -inf chunks.
+  chunked_partials -- pinned through the chunked + merged == unchunked check.
+  last_token_gather -- pinned: golden indices for the tiny workload.
+"""
+from .attention import (  # noqa: F401
+    varlen_attention,
+    varlen_attention_rows,
+    attn_update,
+    last_token_gather,
+    chunked_partials,
+)

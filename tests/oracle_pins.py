@@ -1,0 +1,341 @@
+"""Checks that pin the CPU oracle to facts outside itself.
+
+Each ``check_*`` takes the oracle module and raises AssertionError on a
+mismatch. test_oracle_pins.py runs them against the real oracle;
+test_oracle_mutants.py plants mistakes in the oracle and requires that some
+check fails for each planted mistake.
+
+Pins come from: hand-worked golden values (tests/golden/, each citing the
+page passage it follows), brute force written independently with math.fsum,
+torch's fp64 CPU scaled_dot_product_attention on padded per-sequence
+inputs, closed forms and invariants of softmax attention and of the merge.
+"""
+from __future__ import annotations
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _f(x):
+    if isinstance(x, str):
+        return float(x)          # "-inf" / "inf"
+    if isinstance(x, list):
+        return [_f(e) for e in x]
+    return x
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as fh:
+        return json.load(fh)
+
+
+def _cu(lengths):
+    return np.concatenate([[0], np.cumsum(np.asarray(lengths, dtype=np.int64))]).astype(np.int32)
+
+
+def _same(a, b, tol):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, (a.shape, b.shape)
+    inf_a, inf_b = np.isinf(a), np.isinf(b)
+    assert np.array_equal(inf_a, inf_b), "infinite entries differ"
+    assert np.array_equal(a[inf_a], b[inf_b]), "signs of infinite entries differ"
+    fin = ~inf_a
+    assert not np.isnan(a).any() and not np.isnan(b).any(), "NaN"
+    if fin.any():
+        err = np.abs(a[fin] - b[fin])
+        bound = tol + tol * np.abs(b[fin])
+        assert (err <= bound).all(), f"max err {err.max():.3e}"
+
+
+# ---------------------------------------------------------------- random cases
+
+def _rand_case(rng, batch, max_len, hq, hkv, d, allow_unequal=True, allow_empty=False):
+    lo = 0 if allow_empty else 1
+    lq = rng.integers(lo, max_len + 1, batch)
+    lk = rng.integers(lo, max_len + 1, batch) if allow_unequal else lq.copy()
+    tq, tk = int(lq.sum()), int(lk.sum())
+    q = rng.standard_normal((tq, hq, d))
+    k = rng.standard_normal((tk, hkv, d))
+    v = rng.standard_normal((tk, hkv, d))
+    return lq, lk, q, k, v
+
+
+def brute_force(q, k, v, lengths_q, lengths_k, hq, hkv, scale, causal, d, dv):
+    """Pure-Python softmax attention from the definition, with math.fsum sums."""
+    cu_q = [0]
+    for x in lengths_q:
+        cu_q.append(cu_q[-1] + int(x))
+    cu_k = [0]
+    for x in lengths_k:
+        cu_k.append(cu_k[-1] + int(x))
+    grp = hq // hkv
+    out = [[[0.0] * dv for _ in range(hq)] for _ in range(cu_q[-1])]
+    lse = [[-math.inf] * hq for _ in range(cu_q[-1])]
+    for b in range(len(lengths_q)):
+        lq, lk = cu_q[b + 1] - cu_q[b], cu_k[b + 1] - cu_k[b]
+        for h in range(hq):
+            kvh = h // grp
+            for i in range(lq):
+                t = cu_q[b] + i
+                keys = [j for j in range(lk) if (not causal) or j <= i + lk - lq]
+                if not keys:
+                    continue
+                s = {j: scale * math.fsum(q[t][h][x] * k[cu_k[b] + j][kvh][x] for x in range(d))
+                     for j in keys}
+                mx = max(s.values())
+                w = {j: math.exp(s[j] - mx) for j in keys}
+                tot = math.fsum(w.values())
+                for x in range(dv):
+                    out[t][h][x] = math.fsum(w[j] * v[cu_k[b] + j][kvh][x] for j in keys) / tot
+                lse[t][h] = mx + math.log(tot)
+    return np.array(out, dtype=np.float64).reshape(cu_q[-1], hq, dv), \
+        np.array(lse, dtype=np.float64).reshape(cu_q[-1], hq)
+
+
+def check_golden_attention(orc):
+    for case in _load("attention_handworked.json")["cases"]:
+        q = np.array(case["q"], dtype=np.float64)
+        k = np.array(case["k"], dtype=np.float64)
+        v = np.array(case["v"], dtype=np.float64)
+        o, lse = orc.varlen_attention(q, k, v, _cu(case["lengths_q"]), _cu(case["lengths_k"]),
+                                      case["num_heads_kv"], case["scale"], case["causal"])
+        _same(o, np.array(_f(case["out"])), 1e-12)
+        _same(lse, np.array(_f(case["lse"])), 1e-12)
+
+
+def check_golden_merge(orc):
+    g = _load("merge_handworked.json")
+    lse = np.array(_f(g["lse"]), dtype=np.float64)
+    go = np.array(g["go"], dtype=np.float64)
+    out, lse_out = orc.attn_update(lse, go, 1)
+    _same(out, np.array(g["out"]), 1e-12)
+    _same(lse_out, np.array(_f(g["lse_out"])), 1e-12)
+    out0, none = orc.attn_update(lse, go, 0)
+    assert none is None
+    _same(out0, np.array(g["out"]), 1e-12)
+
+
+def check_golden_gather(orc):
+    g = _load("gather_tiny.json")
+    assert _cu(g["lengths"]).tolist() == g["cu_seqlens"]
+    x = np.arange(g["cu_seqlens"][-1] * 3, dtype=np.float64).reshape(-1, 3)
+    got = orc.last_token_gather(x, np.array(g["cu_seqlens"], dtype=np.int32))
+    assert np.array_equal(got[:, 0] / 3, np.array(g["last_token_indices"], dtype=np.float64))
+
+
+def check_brute_force(orc, n_cases=40, seed=11):
+    rng = np.random.default_rng(seed)
+    for _ in range(n_cases):
+        batch = int(rng.integers(1, 4))
+        hkv = int(rng.integers(1, 3))
+        hq = hkv * int(rng.integers(1, 3))
+        d = int(rng.integers(1, 5))
+        causal = bool(rng.integers(0, 2))
+        scale = float(rng.uniform(0.2, 1.5))
+        lq, lk, q, k, v = _rand_case(rng, batch, 5, hq, hkv, d, allow_unequal=True, allow_empty=True)
+        o_b, lse_b = brute_force(q.tolist(), k.tolist(), v.tolist(), lq, lk, hq, hkv, scale, causal, d, d)
+        o, lse = orc.varlen_attention(q, k, v, _cu(lq), _cu(lk), hkv, scale, causal)
+        _same(o, o_b, 1e-12)
+        _same(lse, lse_b, 1e-12)
+
+
+def check_torch_sdpa(orc, seed=5):
+    """torch CPU fp64 SDPA on padded per-sequence BNSD with repeat-interleaved K/V."""
+    import torch
+    import torch.nn.functional as F
+    rng = np.random.default_rng(seed)
+    for causal, (hq, hkv) in itertools.product([True, False], [(4, 2), (6, 3), (2, 2)]):
+        d = 8
+        lq = rng.integers(1, 12, 3)
+        lk = lq + rng.integers(0, 4, 3)      # Lk >= Lq so no row is fully masked
+        q = rng.standard_normal((int(lq.sum()), hq, d))
+        k = rng.standard_normal((int(lk.sum()), hkv, d))
+        v = rng.standard_normal((int(lk.sum()), hkv, d))
+        scale = 0.37
+        o, lse = orc.varlen_attention(q, k, v, _cu(lq), _cu(lk), hkv, scale, causal)
+        cq, ck = _cu(lq), _cu(lk)
+        for b in range(3):
+            qb = torch.from_numpy(q[cq[b]:cq[b + 1]]).transpose(0, 1).unsqueeze(0)      # [1,Hq,Lq,D]
+            kb = torch.from_numpy(k[ck[b]:ck[b + 1]]).repeat_interleave(hq // hkv, dim=1)
+            vb = torch.from_numpy(v[ck[b]:ck[b + 1]]).repeat_interleave(hq // hkv, dim=1)
+            kb = kb.transpose(0, 1).unsqueeze(0).contiguous()
+            vb = vb.transpose(0, 1).unsqueeze(0).contiguous()
+            lqb, lkb = int(lq[b]), int(lk[b])
+            ii = torch.arange(lqb)[:, None]
+            jj = torch.arange(lkb)[None, :]
+            allow = (jj <= ii + (lkb - lqb)) if causal else torch.ones(lqb, lkb, dtype=torch.bool)
+            ref = F.scaled_dot_product_attention(qb, kb, vb, attn_mask=allow, scale=scale)
+            sc = scale * (qb @ kb.transpose(-1, -2))
+            sc = sc.masked_fill(~allow, float("-inf"))
+            ref_lse = torch.logsumexp(sc, dim=-1)                                           # [1,Hq,Lq]
+            _same(o[cq[b]:cq[b + 1]], ref[0].transpose(0, 1).numpy(), 1e-10)
+            _same(lse[cq[b]:cq[b + 1]], ref_lse[0].transpose(0, 1).numpy(), 1e-10)
+
+
+def check_closed_forms(orc, seed=7):
+    rng = np.random.default_rng(seed)
+    hq, hkv, d = 4, 2, 6
+    grp = hq // hkv
+    lq = np.array([5, 9, 1]); lk = np.array([7, 9, 3])
+    cq, ck = _cu(lq), _cu(lk)
+    k = rng.standard_normal((int(lk.sum()), hkv, d))
+    v = rng.standard_normal((int(lk.sum()), hkv, d))
+    # (1) Q = 0: uniform weights over visible keys -> mean of visible V, lse = ln(#visible)
+    q0 = np.zeros((int(lq.sum()), hq, d))
+    o, lse = orc.varlen_attention(q0, k, v, cq, ck, hkv, 0.5, True)
+    for b in range(3):
+        for i in range(int(lq[b])):
+            nvis = min(int(lk[b]), max(0, i + 1 + int(lk[b]) - int(lq[b])))
+            for h in range(hq):
+                t = cq[b] + i
+                if nvis == 0:
+                    assert lse[t, h] == -np.inf and not o[t, h].any()
+                    continue
+                exp_o = v[ck[b]:ck[b] + nvis, h // grp].mean(axis=0)
+                _same(o[t, h], exp_o, 1e-12)
+                _same(lse[t, h], math.log(nvis), 1e-12)
+    # (2) causal, Lq = Lk: row 0 sees only key 0 -> O = V[0], lse = scale q0.k0
+    q = rng.standard_normal((int(lq.sum()), hq, d))
+    sq = np.array([4, 6]); cs = _cu(sq)
+    qs = rng.standard_normal((10, hq, d)); ks = rng.standard_normal((10, hkv, d)); vs = rng.standard_normal((10, hkv, d))
+    o, lse = orc.varlen_attention(qs, ks, vs, cs, cs, hkv, 0.3, True)
+    for b in range(2):
+        t = cs[b]
+        for h in range(hq):
+            _same(o[t, h], vs[t, h // grp], 1e-12)
+            _same(lse[t, h], 0.3 * float(qs[t, h] @ ks[t, h // grp]), 1e-12)
+    # (3) V constant per kv head -> O equals that constant on every row with a visible key
+    vc = np.broadcast_to(np.array([1.5, -2.0])[None, :, None], v.shape).copy()
+    o, lse = orc.varlen_attention(q, k, vc, cq, ck, hkv, 0.9, False)
+    for h in range(hq):
+        _same(o[:, h, :], np.full((int(lq.sum()), d), [1.5, -2.0][h // grp]), 1e-12)
+    # (4) one key: O = V0, lse = s0
+    q1 = rng.standard_normal((3, hq, d)); k1 = rng.standard_normal((1, hkv, d)); v1 = rng.standard_normal((1, hkv, d))
+    o, lse = orc.varlen_attention(q1, k1, v1, np.array([0, 3]), np.array([0, 1]), hkv, 0.7, False)
+    for h in range(hq):
+        _same(o[:, h], np.repeat(v1[0:1, h // grp], 3, axis=0), 1e-12)
+        _same(lse[:, h], 0.7 * (q1[:, h] @ k1[0, h // grp]), 1e-12)
+
+
+def check_merge_invariants(orc, seed=3):
+    rng = np.random.default_rng(seed)
+    for causal, sp in itertools.product([True, False], [1, 2, 3, 8]):
+        hq, hkv, d = 4, 2, 5
+        lq = np.array([6, 13, 1, 9]); lk = lq.copy()
+        if not causal:
+            lk = np.array([7, 13, 11, 2])
+        q = rng.standard_normal((int(lq.sum()), hq, d))
+        k = rng.standard_normal((int(lk.sum()), hkv, d))
+        v = rng.standard_normal((int(lk.sum()), hkv, d))
+        o, lse = orc.varlen_attention(q, k, v, _cu(lq), _cu(lk), hkv, 0.4, causal)
+        lse_c, go_c = orc.chunked_partials(q, k, v, _cu(lq), _cu(lk), hkv, 0.4, causal, sp)
+        # (5) chunked + merged = unchunked
+        out_m, lse_m = orc.attn_update(lse_c, go_c, 1)
+        _same(out_m, o.reshape(-1, d), 1e-11)
+        _same(lse_m, lse.reshape(-1), 1e-11)
+        # (9) chunk order does not matter
+        perm = rng.permutation(sp)
+        out_p, lse_p = orc.attn_update(lse_c[perm], go_c[perm], 1)
+        _same(out_p, out_m, 1e-12)
+        _same(lse_p, lse_m, 1e-12)
+    # (8) sp = 1 is the identity
+    lse1 = rng.standard_normal((1, 10)); go1 = rng.standard_normal((1, 10, 3))
+    out1, l1 = orc.attn_update(lse1, go1, 1)
+    _same(out1, go1[0], 1e-13)
+    _same(l1, lse1[0], 1e-13)
+    # (10) a chunk with lse = -inf contributes nothing, whatever its O
+    lse2 = np.concatenate([lse1, np.full((1, 10), -np.inf)], axis=0)
+    go2 = np.concatenate([go1, 1e6 * rng.standard_normal((1, 10, 3))], axis=0)
+    out2, l2 = orc.attn_update(lse2, go2, 1)
+    _same(out2, go1[0], 1e-13)
+    _same(l2, lse1[0], 1e-13)
+    # merging two equal partials adds ln 2 to lse and keeps O
+    out3, l3 = orc.attn_update(np.concatenate([lse1, lse1]), np.concatenate([go1, go1]), 1)
+    _same(out3, go1[0], 1e-12)
+    _same(l3, lse1[0] + math.log(2.0), 1e-12)
+
+
+def check_attention_invariants(orc, seed=9):
+    rng = np.random.default_rng(seed)
+    hq, hkv, d = 6, 2, 7
+    grp = hq // hkv
+    lq = np.array([3, 10, 1, 6]); lk = np.array([5, 10, 4, 6])
+    cq, ck = _cu(lq), _cu(lk)
+    q = rng.standard_normal((int(lq.sum()), hq, d))
+    k = rng.standard_normal((int(lk.sum()), hkv, d))
+    v = rng.standard_normal((int(lk.sum()), hkv, d))
+    for causal in (True, False):
+        o, lse = orc.varlen_attention(q, k, v, cq, ck, hkv, 0.45, causal)
+        # (6) packed TND = each sequence alone
+        for b in range(4):
+            ob, lb = orc.varlen_attention(q[cq[b]:cq[b + 1]], k[ck[b]:ck[b + 1]], v[ck[b]:ck[b + 1]],
+                                          np.array([0, lq[b]]), np.array([0, lk[b]]), hkv, 0.45, causal)
+            _same(o[cq[b]:cq[b + 1]], ob, 1e-13)
+            _same(lse[cq[b]:cq[b + 1]], lb, 1e-13)
+        # (7) GQA = MHA on K/V repeated along the head axis (repeat_interleave(G, dim=1))
+        om, lm = orc.varlen_attention(q, np.repeat(k, grp, axis=1), np.repeat(v, grp, axis=1),
+                                      cq, ck, hq, 0.45, causal)
+        _same(o, om, 1e-13)
+        _same(lse, lm, 1e-13)
+        # (11) K -> K + u per kv head: O unchanged, lse shifts by scale * q.u
+        u = rng.standard_normal((hkv, d))
+        ou, lu = orc.varlen_attention(q, k + u[None], v, cq, ck, hkv, 0.45, causal)
+        shift = 0.45 * np.einsum("thd,hd->th", q, np.repeat(u, grp, axis=0))
+        fin = np.isfinite(lse)
+        _same(ou, o, 1e-11)
+        _same(lu[fin], (lse + shift)[fin], 1e-11)
+        # (12) scale folded into Q
+        os_, ls_ = orc.varlen_attention(0.45 * q, k, v, cq, ck, hkv, 1.0, causal)
+        _same(os_, o, 1e-12)
+        _same(ls_, lse, 1e-12)
+        # (13) max_j s_j <= lse <= max_j s_j + ln(#visible)
+        for b in range(4):
+            for i in range(int(lq[b])):
+                vis = [j for j in range(int(lk[b])) if (not causal) or j <= i + lk[b] - lq[b]]
+                for h in range(hq):
+                    t = cq[b] + i
+                    if not vis:
+                        assert lse[t, h] == -np.inf
+                        continue
+                    s = [0.45 * float(q[t, h] @ k[ck[b] + j, h // grp]) for j in vis]
+                    assert max(s) - 1e-12 <= lse[t, h] <= max(s) + math.log(len(vis)) + 1e-12
+        # (14) sequence order in the pack does not matter
+        perm = np.array([2, 0, 3, 1])
+        qp = np.concatenate([q[cq[b]:cq[b + 1]] for b in perm])
+        kp = np.concatenate([k[ck[b]:ck[b + 1]] for b in perm])
+        vp = np.concatenate([v[ck[b]:ck[b + 1]] for b in perm])
+        op, lp = orc.varlen_attention(qp, kp, vp, _cu(lq[perm]), _cu(lk[perm]), hkv, 0.45, causal)
+        _same(op, np.concatenate([o[cq[b]:cq[b + 1]] for b in perm]), 1e-13)
+        _same(lp, np.concatenate([lse[cq[b]:cq[b + 1]] for b in perm]), 1e-13)
+
+
+def check_rows_subset(orc, seed=13):
+    """Selected-token evaluation equals the same rows of the whole-batch result."""
+    rng = np.random.default_rng(seed)
+    lq = np.array([4, 9, 2]); lk = np.array([4, 12, 2])
+    q = rng.standard_normal((15, 4, 3)); k = rng.standard_normal((18, 2, 3)); v = rng.standard_normal((18, 2, 3))
+    o, lse = orc.varlen_attention(q, k, v, _cu(lq), _cu(lk), 2, 0.8, True)
+    tok = np.array([14, 0, 7, 4, 13])
+    os_, ls_ = orc.varlen_attention_rows(q, k, v, _cu(lq), _cu(lk), 2, 0.8, True, tokens=tok)
+    _same(os_, o[tok], 1e-14)
+    _same(ls_, lse[tok], 1e-14)
+
+
+ALL_CHECKS = [
+    check_golden_attention,
+    check_golden_merge,
+    check_golden_gather,
+    check_brute_force,
+    check_torch_sdpa,
+    check_closed_forms,
+    check_merge_invariants,
+    check_attention_invariants,
+    check_rows_subset,
+]

@@ -1,0 +1,58 @@
+"""Plant one mistake at a time in a copy of the oracle; some pin must catch each.
+
+Mistakes are planted on the CPU in a private copy of the oracle's source text
+(the real module is untouched). A mutant that every pin accepts would mean
+the pins cannot tell that mistake from the definition.
+"""
+import os
+import types
+
+import pytest
+
+from tests import oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "attention.py")
+
+MUTANTS = {
+    "gqa_modulo_mapping": ("g = h // grp", "g = h % hkv"),
+    "causal_top_left": ("vis &= j <= (i_pos[:, None] + (lk - lq))", "vis &= j <= i_pos[:, None]"),
+    "causal_diagonal_masked": ("vis &= j <= (i_pos[:, None] + (lk - lq))", "vis &= j < (i_pos[:, None] + (lk - lq))"),
+    "scale_dropped": ("s = scale * (q_rows @ k_seq.T)", "s = (q_rows @ k_seq.T)"),
+    "lse_without_max": ("lse[has] = m[has] + np.log(l_sum[has])", "lse[has] = np.log(l_sum[has])"),
+    "lse_log2": ("lse[has] = m[has] + np.log(l_sum[has])", "lse[has] = m[has] + np.log2(l_sum[has])"),
+    "v_rows_reversed": ("o = (e @ v_seq)", "o = (e @ v_seq[::-1])"),
+    "head_row_swap": ("out[rows, h, :] = o_h", "out[rows, (h + 1) % hq, :] = o_h"),
+    "merge_unnormalised": ("np.exp(lse - np.where(live, lse_m, 0.0)[None, :])", "np.exp(lse - safe_max[None, :])"),
+    "merge_min_not_max": ("lse_max = lse.max(axis=0)", "lse_max = lse.min(axis=0)"),
+    "merge_lse_no_log": ("lse_m = np.where(live, safe_max + np.log(np.where(live, ssum, 1.0)), -np.inf)",
+                         "lse_m = np.where(live, safe_max + np.where(live, ssum, 1.0), -np.inf)"),
+    "chunk_drops_key": ("return (c * lk) // sp, ((c + 1) * lk) // sp", "return (c * lk) // sp, max((c * lk) // sp, ((c + 1) * lk) // sp - 1)"),
+    "gather_first_token": ("idx = cu[1:] - 1", "idx = cu[:-1]"),
+}
+
+
+def _mutant_module(old, new):
+    with open(SRC) as fh:
+        src = fh.read()
+    assert src.count(old) == 1, f"mutation site not found exactly once: {old!r}"
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(src.replace(old, new), SRC + " (mutant)", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name):
+    mod = _mutant_module(*MUTANTS[name])
+    caught = []
+    for check in pins.ALL_CHECKS:
+        try:
+            check(mod)
+        except Exception as exc:  # noqa: BLE001 - any failure counts as caught
+            caught.append((check.__name__, type(exc).__name__))
+    assert caught, f"no pin catches mutant {name}"
+
+
+def test_unmutated_copy_passes():
+    mod = _mutant_module("import numpy as np", "import numpy as np")
+    for check in pins.ALL_CHECKS:
+        check(mod)

@@ -1,0 +1,219 @@
+"""Seeded synthetic inputs for varlen attention and the AttentionUpdate merge.
+
+This module only draws numbers: sequence lengths, Q/K/V values and the
+chunk boundaries a caller asks for. It holds none of the attention or merge
+arithmetic, so the CPU oracle and the HIP path can both be fed from it
+without sharing any of the method.
+
+Shapes follow the workloads the pages describe:
+  * "From GPU to NPU: Qwen3-Embedding on Ascend", core optimisation 1 (TND
+    format): all tokens of a batch flattened to [total_tokens, heads, head_dim],
+    sequence boundaries in an int32 cu_seqlens of length B+1.
+  * same page, core optimisation 5 (FIA, native GQA): 16 query heads, 8 kv
+    heads, head_dim 128 for the embedding model.
+  * "Qwen3-MoE low-latency inference on Atlas A3", attention TP section: the
+    same fused attention op serves prefill and decode.
+
+Random draws use numpy's PCG64 (default_rng). Draw order per workload:
+lengths, then Q, then K, then V. Values are i.i.d. N(0,1) drawn in fp32; for
+bf16 workloads they are rounded to bf16 (round to nearest even) and both
+sides receive the rounded values.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+__all__ = [
+    "Workload",
+    "round_to_bf16",
+    "bf16_bits",
+    "make_workload",
+    "make_custom",
+    "chunk_bounds",
+    "WORKLOAD_NAMES",
+]
+
+
+def round_to_bf16(x: np.ndarray) -> np.ndarray:
+    """Round fp32 values to the nearest bf16 (ties to even); returns fp32 holding them."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32)
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """The upper 16 bits of fp32 values that are already bf16-exact, as uint16."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32)
+    if np.any(u & 0xFFFF):
+        raise ValueError("values are not bf16-exact; round them first")
+    return (u >> 16).astype(np.uint16)
+
+
+@dataclass
+class Workload:
+    name: str
+    lengths_q: np.ndarray          # int64 [B]
+    lengths_k: np.ndarray          # int64 [B]
+    num_heads_q: int
+    num_heads_kv: int
+    head_dim: int
+    dtype: str                     # "fp32" or "bf16"
+    causal: bool
+    scale: float
+    seed: int
+    q: np.ndarray = field(repr=False, default=None)   # fp32 [Tq, Hq, D]
+    k: np.ndarray = field(repr=False, default=None)   # fp32 [Tk, Hkv, D]
+    v: np.ndarray = field(repr=False, default=None)   # fp32 [Tk, Hkv, D]
+
+    @property
+    def batch(self) -> int:
+        return int(len(self.lengths_q))
+
+    @property
+    def cu_seqlens_q(self) -> np.ndarray:
+        return np.concatenate([[0], np.cumsum(self.lengths_q)]).astype(np.int32)
+
+    @property
+    def cu_seqlens_k(self) -> np.ndarray:
+        return np.concatenate([[0], np.cumsum(self.lengths_k)]).astype(np.int32)
+
+    @property
+    def total_q(self) -> int:
+        return int(self.lengths_q.sum())
+
+    @property
+    def total_k(self) -> int:
+        return int(self.lengths_k.sum())
+
+    @property
+    def max_seqlen_q(self) -> int:
+        return int(self.lengths_q.max()) if self.batch else 0
+
+    @property
+    def max_seqlen_k(self) -> int:
+        return int(self.lengths_k.max()) if self.batch else 0
+
+    def with_causal(self, causal: bool) -> "Workload":
+        w = Workload(**{**self.__dict__})
+        w.causal = bool(causal)
+        return w
+
+    def visible_pairs(self) -> int:
+        """Number of (query row, key) pairs the mask leaves visible, per query head.
+
+        Causal masking is aligned bottom-right: query i of a sequence with Lq
+        queries and Lk keys sees key j iff j <= i + Lk - Lq.
+        """
+        total = 0
+        for lq, lk in zip(self.lengths_q.tolist(), self.lengths_k.tolist()):
+            if not self.causal:
+                total += lq * lk
+                continue
+            off = lk - lq
+            for_i = np.clip(np.arange(lq, dtype=np.int64) + off + 1, 0, lk)
+            total += int(for_i.sum())
+        return total
+
+    def useful_flops(self) -> float:
+        """4 * head_dim per visible (query row, query head, key); masked pairs excluded."""
+        return 4.0 * self.head_dim * self.num_heads_q * self.visible_pairs()
+
+    def compulsory_bytes(self, out_bytes_per_elem: int | None = None) -> int:
+        """Q, K, V read once; O and lse written once."""
+        eb = 4 if self.dtype == "fp32" else 2
+        ob = eb if out_bytes_per_elem is None else out_bytes_per_elem
+        tq, tk = self.total_q, self.total_k
+        hq, hkv, d = self.num_heads_q, self.num_heads_kv, self.head_dim
+        return tq * hq * d * eb + 2 * tk * hkv * d * eb + tq * hq * d * ob + tq * hq * 4
+
+
+def _draw_values(rng: np.random.Generator, lq: np.ndarray, lk: np.ndarray,
+                 hq: int, hkv: int, d: int, dtype: str):
+    tq, tk = int(lq.sum()), int(lk.sum())
+    q = rng.standard_normal((tq, hq, d), dtype=np.float32)
+    k = rng.standard_normal((tk, hkv, d), dtype=np.float32)
+    v = rng.standard_normal((tk, hkv, d), dtype=np.float32)
+    if dtype == "bf16":
+        q, k, v = round_to_bf16(q), round_to_bf16(k), round_to_bf16(v)
+    elif dtype != "fp32":
+        raise ValueError(f"unknown dtype {dtype!r}")
+    return q, k, v
+
+
+# name -> (description, default seed)
+WORKLOAD_NAMES = {
+    "tiny_fp32": "4 sequences {17,64,5,128}, Hq=4 Hkv=2 D=64, fp32, causal",
+    "embed_prefill": "64 sequences uniform in [32,512], Hq=16 Hkv=8 D=128, bf16, causal",
+    "long_prefill": "16 sequences log-normal (median 2048, clip [256,8192]), Hq=32 Hkv=8 D=128, bf16, causal",
+    "long_prefill_full": "long_prefill shapes with full (non-causal) masking",
+    "decode": "64 sequences, 1 query each, KV lengths uniform in [1024,32768], Hq=32 Hkv=4 D=128, bf16",
+}
+
+
+def _lengths(name: str, rng: np.random.Generator):
+    if name == "tiny_fp32":
+        lq = np.array([17, 64, 5, 128], dtype=np.int64)
+        return lq, lq.copy()
+    if name == "embed_prefill":
+        lq = rng.integers(32, 513, 64).astype(np.int64)
+        return lq, lq.copy()
+    if name in ("long_prefill", "long_prefill_full"):
+        raw = rng.lognormal(mean=math.log(2048.0), sigma=1.0, size=16)
+        lq = np.clip(np.rint(raw), 256, 8192).astype(np.int64)
+        return lq, lq.copy()
+    if name == "decode":
+        lk = rng.integers(1024, 32769, 64).astype(np.int64)
+        return np.ones(64, dtype=np.int64), lk
+    raise KeyError(name)
+
+
+_SHAPES = {
+    # name: (Hq, Hkv, D, dtype, causal, seed)
+    "tiny_fp32": (4, 2, 64, "fp32", True, 1),
+    "embed_prefill": (16, 8, 128, "bf16", True, 2),
+    "long_prefill": (32, 8, 128, "bf16", True, 3),
+    "long_prefill_full": (32, 8, 128, "bf16", False, 3),
+    "decode": (32, 4, 128, "bf16", True, 4),
+}
+
+
+def make_workload(name: str, seed: int | None = None, values: bool = True) -> Workload:
+    """Build one of the named workloads. ``values=False`` draws only the lengths."""
+    hq, hkv, d, dtype, causal, default_seed = _SHAPES[name]
+    seed = default_seed if seed is None else int(seed)
+    rng = np.random.default_rng(seed)
+    lq, lk = _lengths(name, rng)
+    w = Workload(name=name, lengths_q=lq, lengths_k=lk, num_heads_q=hq, num_heads_kv=hkv,
+                 head_dim=d, dtype=dtype, causal=causal, scale=1.0 / math.sqrt(d), seed=seed)
+    if values:
+        w.q, w.k, w.v = _draw_values(rng, lq, lk, hq, hkv, d, dtype)
+    return w
+
+
+def make_custom(lengths_q, lengths_k=None, num_heads_q=4, num_heads_kv=2, head_dim=64,
+                dtype="fp32", causal=True, scale=None, seed=0, name="custom") -> Workload:
+    """A workload with caller-chosen lengths (e.g. small parity cases and edge cases)."""
+    lq = np.asarray(lengths_q, dtype=np.int64).reshape(-1)
+    lk = lq.copy() if lengths_k is None else np.asarray(lengths_k, dtype=np.int64).reshape(-1)
+    if lq.shape != lk.shape:
+        raise ValueError("lengths_q and lengths_k must have the same number of sequences")
+    rng = np.random.default_rng(seed)
+    q, k, v = _draw_values(rng, lq, lk, num_heads_q, num_heads_kv, head_dim, dtype)
+    sc = 1.0 / math.sqrt(head_dim) if scale is None else float(scale)
+    return Workload(name=name, lengths_q=lq, lengths_k=lk, num_heads_q=num_heads_q,
+                    num_heads_kv=num_heads_kv, head_dim=head_dim, dtype=dtype,
+                    causal=bool(causal), scale=sc, seed=seed, q=q, k=k, v=v)
+
+
+def chunk_bounds(length: int, sp: int) -> list[tuple[int, int]]:
+    """Key range [lo, hi) of each of ``sp`` chunks of a sequence of ``length`` keys.
+
+    Chunk c covers [floor(c*L/sp), floor((c+1)*L/sp)): equal chunks when sp
+    divides L, otherwise sizes differ by at most one.
+    """
+    return [((c * length) // sp, ((c + 1) * length) // sp) for c in range(sp)]
