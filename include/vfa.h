@@ -1,0 +1,151 @@
+/*
+ * vfa.h -- C ABI of libvfa: attention over packed variable-length sequences
+ * and the AttentionUpdate merge, on AMD MI355X (gfx950).
+ *
+ * Conventions shared by every entry point
+ *   - Tensor arguments are DEVICE pointers to contiguous row-major buffers
+ *     that the caller allocates, owns and frees. The library never allocates,
+ *     frees, synchronises or copies device memory to the host, and keeps no
+ *     state between calls (it is reentrant).
+ *   - `stream` is a hipStream_t (NULL = the null stream). Work is enqueued
+ *     on it asynchronously; results are ready when the stream reaches them.
+ *   - Sizes and flags are HOST values. Every condition that can be checked
+ *     from them is checked before anything is launched; a failed check
+ *     returns its status code and launches nothing. After a launch, a HIP
+ *     launch error is reported as VFA_ERR_LAUNCH.
+ *   - Return values are vfa_status codes (0 = success).
+ *
+ * The argument conventions follow the problem as the source pages state it:
+ *   [P1] "From GPU to NPU: Qwen3-Embedding model adaptation and performance
+ *        optimisation on Ascend", core optimisation 1 (TND layout and
+ *        cu_seqlens), section 2.1 (the fused attention call: head count,
+ *        TND layout, softmax scale, per-sequence lengths, causal mask) and
+ *        core optimisation 5 (native GQA through num_heads and
+ *        num_key_value_heads).
+ *   [P2] "Qwen3-MoE low-latency inference on Atlas A3", flash attention
+ *        fused operator section (one op for prefill and decode).
+ *   [P4] "attention_update operator optimisation practice", operator
+ *        function description (the merge formula) and the InferShape,
+ *        ACLNN and op-plugin sections (plain-tensor inputs, sp read from
+ *        dim 0, output shapes and dtypes, update_type).
+ */
+#ifndef VFA_H
+#define VFA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define VFA_ABI_VERSION 1
+
+typedef enum vfa_status {
+  VFA_OK = 0,
+  VFA_ERR_NULL = 1,         /* a required pointer is NULL                          */
+  VFA_ERR_SHAPE = 2,        /* a size or count is out of range or inconsistent     */
+  VFA_ERR_UNSUPPORTED = 3,  /* valid request this build does not implement         */
+  VFA_ERR_WORKSPACE = 4,    /* workspace missing or smaller than the size query    */
+  VFA_ERR_LAUNCH = 5        /* the HIP runtime reported an error at launch         */
+} vfa_status;
+
+typedef enum vfa_dtype {
+  VFA_F32 = 0,
+  VFA_BF16 = 1
+} vfa_dtype;
+
+/* Version of this ABI compiled into the loaded library; a caller compares it
+ * with VFA_ABI_VERSION to detect a stale library picked up from another path
+ * (the failure mode [P4]'s troubleshooting section describes for a
+ * same-named older operator). */
+int32_t vfa_abi_version(void);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* vfa_status_string(int32_t status);
+
+/* Bytes of device workspace varlen_attn_fwd needs for these host sizes.
+ * 0 means no workspace is needed. Same arguments as varlen_attn_fwd. */
+size_t varlen_attn_fwd_workspace_size(int32_t batch, int32_t total_q,
+                                      int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                      int32_t num_heads_q, int32_t num_heads_kv,
+                                      int32_t head_dim);
+
+/* Varlen attention forward ([P1] section 2.1 and core optimisation 5; [P2]).
+ *
+ * For every sequence b (queries cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1,
+ * keys cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1), query head h and query i:
+ *   s_j   = softmax_scale * <q[i, h, :], k[j, h / G, :]>,  G = Hq / Hkv
+ *   vis   = all keys, or with causal != 0 the keys j <= i + Lk_b - Lq_b
+ *           (bottom-right alignment; with Lq_b == Lk_b this is the
+ *           triu(ones, diagonal=1)-is-masked mask of [P1] 2.1)
+ *   out[i, h, :] = sum_vis exp(s_j - M) v[j, h / G, :] / sum_vis exp(s_j - M)
+ *   lse[i, h]    = ln sum_vis exp(s_j)                     (natural log)
+ * A row with no visible key gets out = 0 and lse = -inf.
+ *
+ * q       [total_q, num_heads_q, head_dim]    in_dtype
+ * k, v    [total_k, num_heads_kv, head_dim]   in_dtype
+ * cu_seqlens_q, cu_seqlens_k: device int32 [batch + 1], cu[0] = 0,
+ *         non-decreasing, cu_q[batch] = total_q, cu_k[batch] = total_k.
+ *         Not read on the host and not checked (caller contract).
+ * max_seqlen_q / max_seqlen_k: host upper bounds of the per-sequence
+ *         lengths; they size the launch so that no device-to-host copy of
+ *         cu_seqlens is needed ([P1] core optimisation 1 keeps cu_seqlens
+ *         on the host for the same reason). A bound below a real length
+ *         leaves that sequence's excess rows unwritten.
+ * out     [total_q, num_heads_q, head_dim]    out_dtype
+ * lse     [total_q, num_heads_q]              fp32
+ * workspace / workspace_bytes: device scratch of at least
+ *         varlen_attn_fwd_workspace_size(...) bytes (may be NULL when that
+ *         size is 0). Its contents on entry do not matter.
+ * Supported: head_dim 64 or 128; in bf16 -> out bf16 or fp32; in fp32 ->
+ *         out fp32. num_heads_q % num_heads_kv == 0 and
+ *         num_heads_q / num_heads_kv <= 32.
+ * batch == 0 or total_q == 0 returns VFA_OK and launches nothing.
+ */
+int32_t varlen_attn_fwd(const void* q, const void* k, const void* v, int32_t in_dtype,
+                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                        int32_t batch, int32_t total_q, int32_t total_k,
+                        int32_t max_seqlen_q, int32_t max_seqlen_k,
+                        int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                        float softmax_scale, int32_t causal,
+                        void* out, int32_t out_dtype, float* lse,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* AttentionUpdate merge ([P4], operator function description):
+ *   lse_max = max_i lse[i, r]
+ *   lse_m   = lse_max + ln sum_i exp(lse[i, r] - lse_max)
+ *   out[r, :] = sum_i go[i, r, :] * exp(lse[i, r] - lse_m)
+ * for r in [0, bsh). Chunks with lse = -inf contribute nothing; a row whose
+ * every chunk is -inf gets lse_m = -inf and out = 0.
+ *
+ * lse     [sp, bsh]        fp32 (sp is dim 0, as in [P4]'s plain-tensor form)
+ * go      [sp, bsh, hd]    go_dtype (fp32 or bf16)
+ * out     [bsh, hd]        same dtype as go ([P4] op-plugin section)
+ * lse_out [bsh]            fp32; written only when update_type == 1, and
+ *                          then it must not be NULL; ignored when 0.
+ * Row order is free to the caller; varlen_attn_fwd's partials use
+ * r = token * num_heads_q + head, so its out/lse feed this call directly.
+ * Supported: hd in {64, 128}, 1 <= sp <= 64. bsh == 0 returns VFA_OK.
+ */
+int32_t attn_update(const float* lse, const void* go, int32_t go_dtype,
+                    int32_t sp, int64_t bsh, int32_t hd, int32_t update_type,
+                    void* out, float* lse_out, void* stream);
+
+/* Last-token gather ([P1] core optimisation 1, embed(): x[cu_seqlens[1:] - 1]).
+ *
+ * x       [total, row_elems]   dtype (any packed-token tensor, e.g. the
+ *                              attention output viewed as [total_q, Hq * D])
+ * out     [batch, row_elems]   dtype; row b = x[cu_seqlens[b + 1] - 1]
+ * cu_seqlens: device int32 [batch + 1]. A sequence of length 0 has no last
+ *         token; its output row is written as zeros.
+ * batch == 0 returns VFA_OK.
+ */
+int32_t varlen_last_token_gather(const void* x, int32_t dtype, const int32_t* cu_seqlens,
+                                 int32_t batch, int64_t row_elems, void* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VFA_H */

@@ -1,0 +1,158 @@
+"""The C-ABI library on the CPU: it loads, exports what include/vfa.h declares,
+and rejects bad arguments with the documented status before any launch.
+
+Every call below fails validation on host values, so nothing is launched
+(the pointers passed are dummies that are never dereferenced).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import varlen_flash_attention_amd as vfa
+from varlen_flash_attention_amd import build as vbuild
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vfa.h")
+
+OK, NULL, SHAPE, UNSUP, WS, LAUNCH = 0, 1, 2, 3, 4, 5
+P = 0x10000          # dummy, 16-byte aligned, never dereferenced
+F32, BF16 = 0, 1
+
+
+def declared_functions():
+    with open(HEADER) as fh:
+        text = fh.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"defined"})
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(vfa.library_path()):
+        vbuild.build()
+    return vfa.load_library()
+
+
+def test_exports_match_header(lib):
+    exported = set(vbuild.exported_symbols())
+    declared = set(declared_functions())
+    assert declared, "no functions parsed from the header"
+    assert declared <= exported, f"declared but not exported: {declared - exported}"
+    assert exported <= declared, f"exported but not declared: {exported - declared}"
+
+
+def test_abi_version(lib):
+    assert lib.vfa_abi_version() == vfa._header_abi_version() == 1
+
+
+def test_status_strings(lib):
+    for code in range(6):
+        s = lib.vfa_status_string(code).decode()
+        assert s.startswith("VFA_")
+    assert lib.vfa_status_string(99).decode() == "unknown vfa status"
+
+
+def _fwd(lib, **kw):
+    a = dict(q=P, k=P, v=P, in_dtype=BF16, cu_q=P, cu_k=P, batch=2, total_q=8, total_k=8, max_q=4, max_k=4,
+             hq=4, hkv=2, d=128, scale=0.125, causal=1, out=P, out_dtype=BF16, lse=P, ws=None, ws_bytes=0,
+             stream=None)
+    a.update(kw)
+    return lib.varlen_attn_fwd(a["q"], a["k"], a["v"], a["in_dtype"], a["cu_q"], a["cu_k"], a["batch"],
+                               a["total_q"], a["total_k"], a["max_q"], a["max_k"], a["hq"], a["hkv"], a["d"],
+                               a["scale"], a["causal"], a["out"], a["out_dtype"], a["lse"], a["ws"],
+                               a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=0), OK),                     # empty batch: nothing to do, nothing launched
+    (dict(total_q=0), OK),
+    (dict(batch=0, q=None), OK),
+    (dict(batch=-1), SHAPE),
+    (dict(total_q=-3), SHAPE),
+    (dict(max_q=-1), SHAPE),
+    (dict(q=None), NULL),
+    (dict(k=None), NULL),
+    (dict(v=None), NULL),
+    (dict(cu_q=None), NULL),
+    (dict(cu_k=None), NULL),
+    (dict(out=None), NULL),
+    (dict(lse=None), NULL),
+    (dict(hq=6, hkv=4), SHAPE),              # Hq % Hkv != 0
+    (dict(hq=0), SHAPE),
+    (dict(hkv=0), SHAPE),
+    (dict(causal=2), SHAPE),
+    (dict(max_q=9), SHAPE),                  # bound above the token count
+    (dict(max_q=3), SHAPE),                  # 2 sequences of <= 3 tokens cannot hold 8
+    (dict(d=96), UNSUP),
+    (dict(d=256), UNSUP),
+    (dict(hq=128, hkv=2), UNSUP),            # G = 64 > 32
+    (dict(in_dtype=7), UNSUP),
+    (dict(in_dtype=F32, out_dtype=BF16), UNSUP),
+    (dict(out_dtype=5), UNSUP),
+    (dict(scale=0.0), UNSUP),
+    (dict(scale=-1.0), UNSUP),
+    (dict(scale=float("nan")), UNSUP),
+    (dict(scale=float("inf")), UNSUP),
+    (dict(q=P + 2), UNSUP),                  # not 16-byte aligned
+    (dict(out=P + 8), UNSUP),
+    # decode-shaped call (Lq = 1, long keys) needs a workspace
+    (dict(batch=4, total_q=4, total_k=8192, max_q=1, max_k=4096, hq=32, hkv=4), WS),
+    (dict(batch=4, total_q=4, total_k=8192, max_q=1, max_k=4096, hq=32, hkv=4, ws=P, ws_bytes=16), WS),
+    (dict(batch=4, total_q=4, total_k=8192, max_q=1, max_k=4096, hq=32, hkv=4, ws=P + 4, ws_bytes=1 << 30), WS),
+])
+def test_fwd_validation(lib, kw, code):
+    assert _fwd(lib, **kw) == code
+
+
+def _upd(lib, **kw):
+    a = dict(lse=P, go=P, go_dtype=F32, sp=8, bsh=2048, hd=128, update_type=1, out=P, lse_out=P, stream=None)
+    a.update(kw)
+    return lib.attn_update(a["lse"], a["go"], a["go_dtype"], a["sp"], a["bsh"], a["hd"], a["update_type"],
+                           a["out"], a["lse_out"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(bsh=0), OK),
+    (dict(sp=0), SHAPE),
+    (dict(sp=-2), SHAPE),
+    (dict(bsh=-1), SHAPE),
+    (dict(update_type=2), SHAPE),
+    (dict(lse=None), NULL),
+    (dict(go=None), NULL),
+    (dict(out=None), NULL),
+    (dict(lse_out=None), NULL),              # update_type 1 needs lse_out
+    (dict(hd=96), UNSUP),
+    (dict(go_dtype=3), UNSUP),
+    (dict(go=P + 4), UNSUP),
+    (dict(out=P + 8), UNSUP),
+])
+def test_update_validation(lib, kw, code):
+    assert _upd(lib, **kw) == code
+
+
+@pytest.mark.parametrize("args,code", [
+    ((P, F32, P, 0, 10, P, None), OK),
+    ((P, F32, P, 4, 0, P, None), OK),
+    ((P, F32, P, -1, 10, P, None), SHAPE),
+    ((P, F32, P, 4, -1, P, None), SHAPE),
+    ((None, F32, P, 4, 10, P, None), NULL),
+    ((P, F32, None, 4, 10, P, None), NULL),
+    ((P, F32, P, 4, 10, None, None), NULL),
+    ((P, 9, P, 4, 10, P, None), UNSUP),
+])
+def test_gather_validation(lib, args, code):
+    assert lib.varlen_last_token_gather(*args) == code
+
+
+def test_workspace_size_plan(lib):
+    # Decode-shaped calls (G heads x query tokens <= 16, long keys) get a split-KV workspace of
+    # n_splits * total_q * Hq * (D + 1) fp32 values; prefill-shaped calls need none.
+    ws = lib.varlen_attn_fwd_workspace_size
+    assert ws(64, 64, 1, 32768, 32, 4, 128) == 32 * 64 * 32 * 129 * 4      # 1024-key splits
+    assert ws(2, 2, 1, 4096, 32, 4, 128) == 16 * 2 * 32 * 129 * 4          # 256-key splits for a small batch
+    assert ws(16, 46000, 8192, 8192, 32, 8, 128) == 0                       # prefill
+    assert ws(64, 64, 1, 300, 32, 4, 128) == 0                              # short keys: no split
+    assert ws(8, 24, 3, 8192, 32, 4, 128) == 0                              # 3 tokens x 8 heads > 16 columns
+    assert ws(8, 16, 2, 8192, 16, 2, 64) > 0                                # 2 tokens x 8 heads = 16 columns

@@ -1,0 +1,245 @@
+"""varlen_flash_attention_amd -- varlen attention and the AttentionUpdate merge on MI355X.
+
+A thin ctypes binding over libvfa.so, the C-ABI library built from csrc/
+(HIP kernels for gfx950). The functions here only marshal arguments: they
+check that tensors are on the GPU, contiguous and of a supported dtype,
+allocate outputs (and workspace) with torch on the tensors' device, pass the
+current HIP stream, and raise VfaError on a non-zero status. Every step of
+the computation runs in the library's kernels; there is no CPU fallback. If
+the library has not been built the first call raises.
+
+Entry points (same names as the C ABI in include/vfa.h):
+  varlen_attn_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                  softmax_scale=None, causal=True, out_dtype=None) -> (out, lse)
+  attn_update(lse, go, update_type=1) -> (out, lse_out or None)
+  varlen_last_token_gather(x, cu_seqlens) -> x[cu_seqlens[1:] - 1]
+  varlen_attn_fwd_workspace_size(...) -> bytes
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import re
+
+__all__ = [
+    "VfaError",
+    "library_path",
+    "load_library",
+    "abi_version",
+    "status_string",
+    "varlen_attn_fwd",
+    "varlen_attn_fwd_workspace_size",
+    "attn_update",
+    "varlen_last_token_gather",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_HEADER = os.path.join(os.path.dirname(_PKG), "include", "vfa.h")
+_LIB = None
+
+VFA_F32 = 0
+VFA_BF16 = 1
+
+
+class VfaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = int(status)
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+def library_path() -> str:
+    return os.path.join(_PKG, "libvfa.so")
+
+
+def _header_abi_version() -> int:
+    with open(_HEADER) as fh:
+        m = re.search(r"#define\s+VFA_ABI_VERSION\s+(\d+)", fh.read())
+    if not m:
+        raise RuntimeError("VFA_ABI_VERSION not found in include/vfa.h")
+    return int(m.group(1))
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libvfa.so by absolute path and check its ABI version against the header."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m varlen_flash_attention_amd.build`")
+    lib = ctypes.CDLL(path)
+    c = ctypes
+    lib.vfa_abi_version.restype = c.c_int32
+    lib.vfa_abi_version.argtypes = []
+    lib.vfa_status_string.restype = c.c_char_p
+    lib.vfa_status_string.argtypes = [c.c_int32]
+    lib.varlen_attn_fwd_workspace_size.restype = c.c_size_t
+    lib.varlen_attn_fwd_workspace_size.argtypes = [c.c_int32] * 7
+    lib.varlen_attn_fwd.restype = c.c_int32
+    lib.varlen_attn_fwd.argtypes = [
+        c.c_void_p, c.c_void_p, c.c_void_p, c.c_int32,          # q k v in_dtype
+        c.c_void_p, c.c_void_p,                                 # cu_q cu_k
+        c.c_int32, c.c_int32, c.c_int32, c.c_int32, c.c_int32,  # batch total_q total_k max_q max_k
+        c.c_int32, c.c_int32, c.c_int32,                        # hq hkv d
+        c.c_float, c.c_int32,                                   # scale causal
+        c.c_void_p, c.c_int32, c.c_void_p,                      # out out_dtype lse
+        c.c_void_p, c.c_size_t, c.c_void_p,                     # workspace bytes stream
+    ]
+    lib.attn_update.restype = c.c_int32
+    lib.attn_update.argtypes = [c.c_void_p, c.c_void_p, c.c_int32, c.c_int32, c.c_int64, c.c_int32,
+                                c.c_int32, c.c_void_p, c.c_void_p, c.c_void_p]
+    lib.varlen_last_token_gather.restype = c.c_int32
+    lib.varlen_last_token_gather.argtypes = [c.c_void_p, c.c_int32, c.c_void_p, c.c_int32, c.c_int64,
+                                             c.c_void_p, c.c_void_p]
+    got, want = lib.vfa_abi_version(), _header_abi_version()
+    if got != want:
+        raise RuntimeError(f"{path} has ABI version {got}, include/vfa.h expects {want}: stale library")
+    _LIB = lib
+    return lib
+
+
+def abi_version() -> int:
+    return int(load_library().vfa_abi_version())
+
+
+def status_string(status: int) -> str:
+    try:
+        return load_library().vfa_status_string(int(status)).decode()
+    except Exception:  # noqa: BLE001 - used while formatting an error
+        return "status"
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return VFA_F32
+    if t.dtype == torch.bfloat16:
+        return VFA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; expected float32 or bfloat16")
+
+
+def _check_gpu(name, t, ndim=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (libvfa has no CPU path)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got {t.dim()}")
+
+
+def _stream_ptr(device) -> int:
+    torch = _torch()
+    return int(torch.cuda.current_stream(device).cuda_stream)
+
+
+def varlen_attn_fwd_workspace_size(batch, total_q, max_seqlen_q, max_seqlen_k, num_heads_q, num_heads_kv,
+                                   head_dim) -> int:
+    return int(load_library().varlen_attn_fwd_workspace_size(int(batch), int(total_q), int(max_seqlen_q),
+                                                             int(max_seqlen_k), int(num_heads_q),
+                                                             int(num_heads_kv), int(head_dim)))
+
+
+def varlen_attn_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
+                    softmax_scale: float | None = None, causal: bool = True, out_dtype=None,
+                    out=None, lse=None, workspace=None):
+    """Attention over packed sequences (TND). Returns (out [Tq,Hq,D], lse [Tq,Hq] fp32).
+
+    q [Tq, Hq, D], k / v [Tk, Hkv, D] (bf16 or fp32, same dtype); cu_seqlens_*
+    int32 [B+1] on the GPU. max_seqlen_* are host upper bounds of the lengths.
+    Default scale 1/sqrt(D); default out dtype = input dtype.
+    """
+    torch = _torch()
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_gpu(name, t, 3)
+    for name, t in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        _check_gpu(name, t, 1)
+        if t.dtype != torch.int32:
+            raise TypeError(f"{name} must be int32")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k and v must share one dtype")
+    if k.shape != v.shape:
+        raise ValueError("k and v must have the same shape")
+    if q.shape[2] != k.shape[2]:
+        raise ValueError("q and k must have the same head_dim")
+    tq, hq, d = (int(x) for x in q.shape)
+    tk, hkv = int(k.shape[0]), int(k.shape[1])
+    batch = int(cu_seqlens_q.shape[0]) - 1
+    if int(cu_seqlens_k.shape[0]) != batch + 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+    in_code = _dtype_code(q)
+    odt = q.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((tq, hq, d), dtype=odt, device=q.device)
+    _check_gpu("out", out, 3)
+    out_code = _dtype_code(out)
+    if lse is None:
+        lse = torch.empty((tq, hq), dtype=torch.float32, device=q.device)
+    _check_gpu("lse", lse, 2)
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    ws_bytes = varlen_attn_fwd_workspace_size(batch, tq, max_seqlen_q, max_seqlen_k, hq, hkv, d)
+    if ws_bytes and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if (ws_bytes and workspace is not None) else None
+    st = lib.varlen_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), in_code,
+                             cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(),
+                             batch, tq, tk, int(max_seqlen_q), int(max_seqlen_k), hq, hkv, d,
+                             scale, 1 if causal else 0, out.data_ptr(), out_code, lse.data_ptr(),
+                             ws_ptr, ws_bytes, _stream_ptr(q.device))
+    if st != 0:
+        raise VfaError(st, "varlen_attn_fwd")
+    return out, lse
+
+
+def attn_update(lse, go, update_type: int = 1, out=None, lse_out=None):
+    """Merge sp partials: lse [sp, bsh] fp32, go [sp, bsh, hd] -> (out [bsh, hd], lse_out [bsh] | None)."""
+    torch = _torch()
+    lib = load_library()
+    _check_gpu("lse", lse, 2)
+    _check_gpu("go", go, 3)
+    if lse.dtype != torch.float32:
+        raise TypeError("lse must be float32")
+    sp, bsh = int(lse.shape[0]), int(lse.shape[1])
+    if tuple(go.shape[:2]) != (sp, bsh):
+        raise ValueError(f"go must be [sp, bsh, hd] = [{sp}, {bsh}, hd], got {tuple(go.shape)}")
+    hd = int(go.shape[2])
+    code = _dtype_code(go)
+    if out is None:
+        out = torch.empty((bsh, hd), dtype=go.dtype, device=go.device)
+    _check_gpu("out", out, 2)
+    if update_type == 1 and lse_out is None:
+        lse_out = torch.empty((bsh,), dtype=torch.float32, device=go.device)
+    st = lib.attn_update(lse.data_ptr(), go.data_ptr(), code, sp, bsh, hd, int(update_type), out.data_ptr(),
+                         lse_out.data_ptr() if (update_type == 1 and lse_out is not None) else None,
+                         _stream_ptr(go.device))
+    if st != 0:
+        raise VfaError(st, "attn_update")
+    return out, (lse_out if update_type == 1 else None)
+
+
+def varlen_last_token_gather(x, cu_seqlens, out=None):
+    """x[cu_seqlens[1:] - 1] along dim 0 of a packed-token tensor (rows of empty sequences: zeros)."""
+    torch = _torch()
+    lib = load_library()
+    _check_gpu("x", x)
+    _check_gpu("cu_seqlens", cu_seqlens, 1)
+    if cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    batch = int(cu_seqlens.shape[0]) - 1
+    row = 1
+    for s in x.shape[1:]:
+        row *= int(s)
+    if out is None:
+        out = torch.empty((batch, *x.shape[1:]), dtype=x.dtype, device=x.device)
+    _check_gpu("out", out)
+    st = lib.varlen_last_token_gather(x.data_ptr(), _dtype_code(x), cu_seqlens.data_ptr(), batch, row,
+                                      out.data_ptr(), _stream_ptr(x.device))
+    if st != 0:
+        raise VfaError(st, "varlen_last_token_gather")
+    return out

@@ -1,0 +1,146 @@
+// libvfa C ABI: argument validation, launch planning and dispatch.
+//
+// Plain C++ with no HIP headers: every check here runs on host values only
+// and returns before anything is launched, so the error paths can be tested
+// without a GPU. Kernels are reached through launch.h.
+//
+// The boundary follows the operator conventions of "attention_update operator
+// optimisation practice" (ACLNN and op-plugin sections): plain tensors, sizes
+// taken from the caller, outputs allocated by the caller, a status code, and
+// validation before execution. The attention arguments follow the fused
+// attention call of "From GPU to NPU: Qwen3-Embedding on Ascend" (section 2.1
+// and core optimisation 5: head counts, TND layout, per-sequence lengths,
+// scale, causal flag).
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/vfa.h"
+#include "launch.h"
+
+#define VFA_API extern "C" __attribute__((visibility("default")))
+
+namespace vfa {
+
+// Split-KV (decode) path: only when the queries of one sequence fit the
+// 16-column tile together with the G heads that share a kv head, and the key
+// sets are long enough for splitting to pay. Keys per split start at 1024
+// and halve (down to 256) until there are enough workgroups to fill the chip.
+DecodePlan plan_decode(int batch, int total_q, int max_seqlen_q, int max_seqlen_k, int hq, int hkv,
+                       int head_dim) {
+  DecodePlan p{false, 0, 0, 0};
+  if (batch <= 0 || total_q <= 0 || hq <= 0 || hkv <= 0 || hq % hkv != 0) return p;
+  const int grp = hq / hkv;
+  if (grp > 16 || (long long)max_seqlen_q * grp > 16 || max_seqlen_q < 1) return p;
+  if (max_seqlen_k < 512) return p;
+  int chunk = 1024;
+  while (chunk > 256 && (long long)batch * hkv * ((max_seqlen_k + chunk - 1) / chunk) < 2048) chunk /= 2;
+  p.use = true;
+  p.chunk = chunk;
+  p.n_splits = (max_seqlen_k + chunk - 1) / chunk;
+  p.ws_bytes = (size_t)p.n_splits * (size_t)total_q * (size_t)hq * (size_t)(head_dim + 1) * sizeof(float);
+  return p;
+}
+
+}  // namespace vfa
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace
+
+VFA_API int32_t vfa_abi_version(void) { return VFA_ABI_VERSION; }
+
+VFA_API const char* vfa_status_string(int32_t status) {
+  switch (status) {
+    case VFA_OK: return "VFA_OK: success";
+    case VFA_ERR_NULL: return "VFA_ERR_NULL: a required pointer is NULL";
+    case VFA_ERR_SHAPE: return "VFA_ERR_SHAPE: a size or count is out of range or inconsistent";
+    case VFA_ERR_UNSUPPORTED: return "VFA_ERR_UNSUPPORTED: request not implemented by this build";
+    case VFA_ERR_WORKSPACE: return "VFA_ERR_WORKSPACE: workspace missing or too small";
+    case VFA_ERR_LAUNCH: return "VFA_ERR_LAUNCH: the HIP runtime reported a launch error";
+    default: return "unknown vfa status";
+  }
+}
+
+VFA_API size_t varlen_attn_fwd_workspace_size(int32_t batch, int32_t total_q, int32_t max_seqlen_q,
+                                              int32_t max_seqlen_k, int32_t num_heads_q,
+                                              int32_t num_heads_kv, int32_t head_dim) {
+  const vfa::DecodePlan p =
+      vfa::plan_decode(batch, total_q, max_seqlen_q, max_seqlen_k, num_heads_q, num_heads_kv, head_dim);
+  return p.use ? p.ws_bytes : 0;
+}
+
+VFA_API int32_t varlen_attn_fwd(const void* q, const void* k, const void* v, int32_t in_dtype,
+                                const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t batch,
+                                int32_t total_q, int32_t total_k, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                                float softmax_scale, int32_t causal, void* out, int32_t out_dtype, float* lse,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  if (batch < 0 || total_q < 0 || total_k < 0 || max_seqlen_q < 0 || max_seqlen_k < 0) return VFA_ERR_SHAPE;
+  if (batch == 0 || total_q == 0) return VFA_OK;
+  if (!q || !k || !v || !cu_seqlens_q || !cu_seqlens_k || !out || !lse) return VFA_ERR_NULL;
+  if (num_heads_q <= 0 || num_heads_kv <= 0 || num_heads_q % num_heads_kv != 0) return VFA_ERR_SHAPE;
+  if (causal != 0 && causal != 1) return VFA_ERR_SHAPE;
+  if (max_seqlen_q > total_q || max_seqlen_k > total_k) return VFA_ERR_SHAPE;
+  if ((long long)max_seqlen_q * batch < total_q || (long long)max_seqlen_k * batch < total_k)
+    return VFA_ERR_SHAPE;
+  if (head_dim != 64 && head_dim != 128) return VFA_ERR_UNSUPPORTED;
+  if (num_heads_q / num_heads_kv > 32) return VFA_ERR_UNSUPPORTED;
+  if (in_dtype == VFA_F32) {
+    if (out_dtype != VFA_F32) return VFA_ERR_UNSUPPORTED;
+  } else if (in_dtype == VFA_BF16) {
+    if (out_dtype != VFA_F32 && out_dtype != VFA_BF16) return VFA_ERR_UNSUPPORTED;
+  } else {
+    return VFA_ERR_UNSUPPORTED;
+  }
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return VFA_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return VFA_ERR_UNSUPPORTED;
+
+  vfa::AttnArgs a{};
+  a.q = q; a.k = k; a.v = v;
+  a.cu_q = cu_seqlens_q; a.cu_k = cu_seqlens_k;
+  a.batch = batch; a.total_q = total_q; a.total_k = total_k;
+  a.max_seqlen_q = max_seqlen_q; a.max_seqlen_k = max_seqlen_k;
+  a.hq = num_heads_q; a.hkv = num_heads_kv; a.grp = num_heads_q / num_heads_kv; a.head_dim = head_dim;
+  a.scale = softmax_scale; a.causal = causal;
+  a.out = out; a.out_dtype = out_dtype == VFA_BF16 ? 1 : 0; a.lse = lse;
+  a.workspace = workspace; a.workspace_bytes = workspace_bytes; a.stream = stream;
+
+  if (in_dtype == VFA_F32) return vfa::launch_attn_fwd_f32(a) == 0 ? VFA_OK : VFA_ERR_LAUNCH;
+
+  const vfa::DecodePlan plan =
+      vfa::plan_decode(batch, total_q, max_seqlen_q, max_seqlen_k, num_heads_q, num_heads_kv, head_dim);
+  if (plan.use) {
+    if (!workspace || workspace_bytes < plan.ws_bytes || !aligned16(workspace)) return VFA_ERR_WORKSPACE;
+    return vfa::launch_attn_decode_bf16(a, plan) == 0 ? VFA_OK : VFA_ERR_LAUNCH;
+  }
+  return vfa::launch_attn_fwd_bf16(a) == 0 ? VFA_OK : VFA_ERR_LAUNCH;
+}
+
+VFA_API int32_t attn_update(const float* lse, const void* go, int32_t go_dtype, int32_t sp, int64_t bsh,
+                            int32_t hd, int32_t update_type, void* out, float* lse_out, void* stream) {
+  if (sp < 1 || bsh < 0) return VFA_ERR_SHAPE;
+  if (update_type != 0 && update_type != 1) return VFA_ERR_SHAPE;
+  if (bsh == 0) return VFA_OK;
+  if (!lse || !go || !out) return VFA_ERR_NULL;
+  if (update_type == 1 && !lse_out) return VFA_ERR_NULL;
+  if (hd != 64 && hd != 128) return VFA_ERR_UNSUPPORTED;
+  if (go_dtype != VFA_F32 && go_dtype != VFA_BF16) return VFA_ERR_UNSUPPORTED;
+  if (!aligned16(go) || !aligned16(out)) return VFA_ERR_UNSUPPORTED;
+  return vfa::launch_attn_update(lse, go, go_dtype == VFA_BF16 ? 1 : 0, sp, bsh, hd, update_type, out, lse_out,
+                                 stream) == 0
+             ? VFA_OK
+             : VFA_ERR_LAUNCH;
+}
+
+VFA_API int32_t varlen_last_token_gather(const void* x, int32_t dtype, const int32_t* cu_seqlens, int32_t batch,
+                                         int64_t row_elems, void* out, void* stream) {
+  if (batch < 0 || row_elems < 0) return VFA_ERR_SHAPE;
+  if (batch == 0 || row_elems == 0) return VFA_OK;
+  if (!x || !cu_seqlens || !out) return VFA_ERR_NULL;
+  if (dtype != VFA_F32 && dtype != VFA_BF16) return VFA_ERR_UNSUPPORTED;
+  return vfa::launch_last_token_gather(x, dtype == VFA_F32 ? 4 : 2, cu_seqlens, batch, row_elems, out, stream) == 0
+             ? VFA_OK
+             : VFA_ERR_LAUNCH;
+}

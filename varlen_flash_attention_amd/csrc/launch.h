@@ -1,0 +1,47 @@
+// Host-side launch interface between the C-ABI layer (api.cpp, plain C++)
+// and the HIP kernels. Plain data only: no HIP types cross this header.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace vfa {
+
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int batch, total_q, total_k, max_seqlen_q, max_seqlen_k;
+  int hq, hkv, grp, head_dim;
+  float scale;
+  int causal;
+  void* out;
+  int out_dtype;  // 0 = fp32, 1 = bf16
+  float* lse;
+  void* workspace;
+  size_t workspace_bytes;
+  void* stream;
+};
+
+// Split-KV plan for short query sets against long key sets (decode).
+struct DecodePlan {
+  bool use;          // take the split-KV path
+  int chunk;         // keys per split
+  int n_splits;      // splits per sequence at max_seqlen_k
+  size_t ws_bytes;   // partial O (fp32) + partial lse (fp32)
+};
+DecodePlan plan_decode(int batch, int total_q, int max_seqlen_q, int max_seqlen_k, int hq, int hkv,
+                       int head_dim);
+
+// Each returns 0 on success, -1 if the HIP runtime reported a launch error.
+int launch_attn_fwd_bf16(const AttnArgs& a);
+int launch_attn_decode_bf16(const AttnArgs& a, const DecodePlan& plan);
+int launch_attn_fwd_f32(const AttnArgs& a);
+int launch_attn_update(const float* lse, const void* go, int go_dtype, int sp, int64_t bsh, int hd,
+                       int update_type, void* out, float* lse_out, void* stream);
+int launch_last_token_gather(const void* x, int esize, const int32_t* cu, int batch, int64_t row_elems,
+                             void* out, void* stream);
+
+}  // namespace vfa

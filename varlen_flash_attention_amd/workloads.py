@@ -14,14 +14,18 @@ Shapes follow the workloads the pages describe:
   * "Qwen3-MoE low-latency inference on Atlas A3", attention TP section: the
     same fused attention op serves prefill and decode.
 
-Random draws use numpy's PCG64 (default_rng). Draw order per workload:
-lengths, then Q, then K, then V. Values are i.i.d. N(0,1) drawn in fp32; for
-bf16 workloads they are rounded to bf16 (round to nearest even) and both
-sides receive the rounded values.
+Random draws use numpy's PCG64. Lengths come from default_rng(seed); Q, K
+and V come from the three children of SeedSequence(seed), each tensor drawn
+in blocks of 2^22 values with one spawned PCG64 stream per block (so the
+values do not depend on the thread count). Values are i.i.d. N(0,1) drawn in
+fp32; for bf16 workloads they are rounded to bf16 (round to nearest even) and
+both sides receive the rounded values.
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
 import math
+import os
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -37,21 +41,63 @@ __all__ = [
 ]
 
 
-def round_to_bf16(x: np.ndarray) -> np.ndarray:
-    """Round fp32 values to the nearest bf16 (ties to even); returns fp32 holding them."""
-    x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
-    return u.astype(np.uint32).view(np.float32)
+_BLOCK = 1 << 22          # values per independently seeded block
+_THREADS = min(16, os.cpu_count() or 1)
+
+
+def _round_slice(u: np.ndarray) -> None:
+    lsb = (u >> 16) & 1
+    u += np.uint32(0x7FFF)
+    u += lsb
+    u &= np.uint32(0xFFFF0000)
+
+
+def round_to_bf16(x: np.ndarray, inplace: bool = False) -> np.ndarray:
+    """Round fp32 values to the nearest bf16 (ties to even); returns fp32 holding them.
+
+    Finite inputs only. Works in slices with uint32 arithmetic, on a copy
+    unless ``inplace`` (then x must be a C-contiguous fp32 array).
+    """
+    if inplace:
+        if x.dtype != np.float32 or not x.flags.c_contiguous:
+            raise ValueError("in-place rounding needs a C-contiguous float32 array")
+        y = x
+    else:
+        y = np.array(x, dtype=np.float32, copy=True, order="C")
+    u = y.reshape(-1).view(np.uint32)
+    with cf.ThreadPoolExecutor(_THREADS) as ex:
+        list(ex.map(lambda lo: _round_slice(u[lo:lo + _BLOCK]), range(0, u.size, _BLOCK)))
+    return y
+
+
+def _normal(seq: np.random.SeedSequence, shape) -> np.ndarray:
+    """i.i.d. N(0,1) fp32 of the given shape.
+
+    Block i of _BLOCK consecutive values (in C order) comes from its own PCG64
+    stream seeded by the i-th child of ``seq``, so the values do not depend on
+    how many threads draw them.
+    """
+    out = np.empty(int(np.prod(shape)), dtype=np.float32)
+    n_blocks = (out.size + _BLOCK - 1) // _BLOCK
+    children = seq.spawn(n_blocks)
+
+    def fill(i):
+        lo = i * _BLOCK
+        np.random.Generator(np.random.PCG64(children[i])).standard_normal(
+            out=out[lo:lo + _BLOCK], dtype=np.float32)
+
+    with cf.ThreadPoolExecutor(_THREADS) as ex:
+        list(ex.map(fill, range(n_blocks)))
+    return out.reshape(shape)
 
 
 def bf16_bits(x: np.ndarray) -> np.ndarray:
     """The upper 16 bits of fp32 values that are already bf16-exact, as uint16."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32)
-    if np.any(u & 0xFFFF):
+    halves = x.reshape(-1).view(np.uint16)          # little-endian: (low, high) pairs
+    if halves[0::2].any():
         raise ValueError("values are not bf16-exact; round them first")
-    return (u >> 16).astype(np.uint16)
+    return np.ascontiguousarray(halves[1::2]).reshape(x.shape)
 
 
 @dataclass
@@ -132,14 +178,15 @@ class Workload:
         return tq * hq * d * eb + 2 * tk * hkv * d * eb + tq * hq * d * ob + tq * hq * 4
 
 
-def _draw_values(rng: np.random.Generator, lq: np.ndarray, lk: np.ndarray,
-                 hq: int, hkv: int, d: int, dtype: str):
+def _draw_values(seed: int, lq: np.ndarray, lk: np.ndarray, hq: int, hkv: int, d: int, dtype: str):
+    """Q, K, V from three child seeds of SeedSequence(seed), in that order."""
     tq, tk = int(lq.sum()), int(lk.sum())
-    q = rng.standard_normal((tq, hq, d), dtype=np.float32)
-    k = rng.standard_normal((tk, hkv, d), dtype=np.float32)
-    v = rng.standard_normal((tk, hkv, d), dtype=np.float32)
+    sq, sk, sv = np.random.SeedSequence(seed).spawn(3)
+    q = _normal(sq, (tq, hq, d))
+    k = _normal(sk, (tk, hkv, d))
+    v = _normal(sv, (tk, hkv, d))
     if dtype == "bf16":
-        q, k, v = round_to_bf16(q), round_to_bf16(k), round_to_bf16(v)
+        q, k, v = (round_to_bf16(t, inplace=True) for t in (q, k, v))
     elif dtype != "fp32":
         raise ValueError(f"unknown dtype {dtype!r}")
     return q, k, v
@@ -191,7 +238,7 @@ def make_workload(name: str, seed: int | None = None, values: bool = True) -> Wo
     w = Workload(name=name, lengths_q=lq, lengths_k=lk, num_heads_q=hq, num_heads_kv=hkv,
                  head_dim=d, dtype=dtype, causal=causal, scale=1.0 / math.sqrt(d), seed=seed)
     if values:
-        w.q, w.k, w.v = _draw_values(rng, lq, lk, hq, hkv, d, dtype)
+        w.q, w.k, w.v = _draw_values(seed, lq, lk, hq, hkv, d, dtype)
     return w
 
 
@@ -202,8 +249,7 @@ def make_custom(lengths_q, lengths_k=None, num_heads_q=4, num_heads_kv=2, head_d
     lk = lq.copy() if lengths_k is None else np.asarray(lengths_k, dtype=np.int64).reshape(-1)
     if lq.shape != lk.shape:
         raise ValueError("lengths_q and lengths_k must have the same number of sequences")
-    rng = np.random.default_rng(seed)
-    q, k, v = _draw_values(rng, lq, lk, num_heads_q, num_heads_kv, head_dim, dtype)
+    q, k, v = _draw_values(seed, lq, lk, num_heads_q, num_heads_kv, head_dim, dtype)
     sc = 1.0 / math.sqrt(head_dim) if scale is None else float(scale)
     return Workload(name=name, lengths_q=lq, lengths_k=lk, num_heads_q=num_heads_q,
                     num_heads_kv=num_heads_kv, head_dim=head_dim, dtype=dtype,
