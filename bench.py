@@ -1,0 +1,291 @@
+#!/usr/bin/env python3
+"""Benchmark of the varlen attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extra]
+
+A step is one varlen_attn_fwd call over the long-prefill workload (16
+sequences, log-normal lengths with median 2048 clipped to [256, 8192],
+Hq=32, Hkv=8, D=128, bf16, causal), inputs already resident in HBM. The
+headline value is useful TFLOP/s: 4 * D FLOPs per visible (query row, query
+head, key), masked pairs excluded. One JSON line is printed.
+
+Extra fields (not the headline): the embedding-style prefill with the
+last-token gather, the same long prefill without masking, decode against
+long KV sets, and the attn_update merge of the chunked-context config
+(sp=8, bsh=2048, hd=128, fp32) timed with caches flushed before every rep.
+
+"roofline" is the attention kernel's achieved useful FLOP rate (per-launch
+HIP-event durations on the launch stream) against the bf16 dense MFMA peak;
+"cpu_baseline" is the fp64 CPU oracle timed on a bounded sample of the same
+workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_bf16_long_prefill_traffic.json")
+KERNEL_SOURCE = os.path.join(ROOT, "varlen_flash_attention_amd", "csrc", "attn_fwd_bf16.hip")
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def device_inputs(w, torch):
+    import numpy as np
+    from varlen_flash_attention_amd.workloads import bf16_bits
+
+    def dev(x):
+        return torch.from_numpy(bf16_bits(x).view(np.int16)).cuda().view(torch.bfloat16)
+
+    return dict(q=dev(w.q), k=dev(w.k), v=dev(w.v), cu_q=torch.from_numpy(w.cu_seqlens_q).cuda(),
+                cu_k=torch.from_numpy(w.cu_seqlens_k).cuda())
+
+
+def time_calls(fn, reps, warmup, torch, flush=None):
+    """Per-call durations (ms) from HIP events on the current stream."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = []
+    for _ in range(reps):
+        if flush is not None:
+            flush()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        fn()
+        e.record()
+        ev.append((s, e))
+    torch.cuda.synchronize()
+    return [s.elapsed_time(e) for s, e in ev]
+
+
+def median(xs):
+    ys = sorted(xs)
+    n = len(ys)
+    return ys[n // 2] if n % 2 else 0.5 * (ys[n // 2 - 1] + ys[n // 2])
+
+
+def attn_case(vfa, torch, w, reps=20, warmup=3, gather=False):
+    d = device_inputs(w, torch)
+    out = torch.empty((w.total_q, w.num_heads_q, w.head_dim), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w.total_q, w.num_heads_q), dtype=torch.float32, device="cuda")
+    ws_bytes = vfa.varlen_attn_fwd_workspace_size(w.batch, w.total_q, w.max_seqlen_q, w.max_seqlen_k,
+                                                  w.num_heads_q, w.num_heads_kv, w.head_dim)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    last = torch.empty((w.batch, w.num_heads_q, w.head_dim), dtype=torch.bfloat16, device="cuda")
+
+    def call():
+        vfa.varlen_attn_fwd(d["q"], d["k"], d["v"], d["cu_q"], d["cu_k"], w.max_seqlen_q, w.max_seqlen_k,
+                            softmax_scale=w.scale, causal=w.causal, out=out, lse=lse, workspace=ws)
+        if gather:
+            vfa.varlen_last_token_gather(out, d["cu_q"], out=last)
+
+    ms = time_calls(call, reps, warmup, torch)
+    t = median(ms)
+    flops = w.useful_flops()
+    byt = w.compulsory_bytes()
+    res = {
+        "ms_median": round(t, 4), "ms_p10": round(sorted(ms)[len(ms) // 10], 4),
+        "ms_p90": round(sorted(ms)[(9 * len(ms)) // 10], 4),
+        "useful_tflops": round(flops / t / 1e9, 2), "frac_bf16_peak": round(flops / t / 1e9 / PEAK_BF16_TFLOPS, 4),
+        "compulsory_gb_per_s": round(byt / t / 1e6, 1), "frac_hbm_peak": round(byt / t / 1e6 / PEAK_HBM_GBPS, 4),
+        "useful_gflop": round(flops / 1e9, 3), "compulsory_mb": round(byt / 1e6, 2),
+        "total_q": w.total_q, "total_k": w.total_k, "batch": w.batch, "seed": w.seed,
+    }
+    del d, out, lse, ws, last
+    torch.cuda.empty_cache()
+    return res
+
+
+def merge_case(vfa, torch, reps=100, warmup=5):
+    """attn_update on the chunked-context merge shape, partials from the decode workload's chunks."""
+    import numpy as np
+    sp, bsh, hd = 8, 64 * 32, 128
+    rng = np.random.default_rng(5)
+    lse = torch.from_numpy(rng.normal(8.0, 2.0, (sp, bsh)).astype(np.float32)).cuda()
+    go = torch.from_numpy(rng.standard_normal((sp, bsh, hd)).astype(np.float32)).cuda()
+    out = torch.empty((bsh, hd), dtype=torch.float32, device="cuda")
+    lse_out = torch.empty((bsh,), dtype=torch.float32, device="cuda")
+    algo_bytes = sp * bsh * (hd + 1) * 4 + bsh * (hd + 1) * 4            # 9,510,912 B
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+
+    def flush():
+        scratch.fill_(1)        # 1 GiB write evicts L2 and the infinity cache
+
+    def call():
+        vfa.attn_update(lse, go, 1, out=out, lse_out=lse_out)
+
+    cold = time_calls(call, reps, warmup, torch, flush=flush)
+    warm = time_calls(call, reps, warmup, torch)
+    res = {}
+    for name, ms in (("cold", cold), ("warm", warm)):
+        t = median(ms)
+        res[name] = {"us_median": round(t * 1e3, 3), "gb_per_s": round(algo_bytes / t / 1e6, 1),
+                     "frac_hbm_peak": round(algo_bytes / t / 1e6 / PEAK_HBM_GBPS, 4)}
+    res["algorithmic_bytes"] = algo_bytes
+    res["shape"] = {"sp": sp, "bsh": bsh, "hd": hd, "dtype": "fp32"}
+    del scratch
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(w, budget_s=12.0):
+    """The fp64 oracle on a bounded, seeded sample of query tokens of the same workload."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    rng = np.random.default_rng(123)
+    order = rng.permutation(w.total_q)
+    cu = w.cu_seqlens_q.astype(np.int64)
+    seq_of = np.searchsorted(cu, order, side="right") - 1
+    done, flops, t0 = 0, 0.0, time.perf_counter()
+    while done < len(order) and time.perf_counter() - t0 < budget_s:
+        toks = np.sort(order[done:done + 64])
+        oracle.varlen_attention_rows(w.q, w.k, w.v, w.cu_seqlens_q, w.cu_seqlens_k, w.num_heads_kv, w.scale,
+                                     w.causal, tokens=toks)
+        for t, b in zip(order[done:done + 64], seq_of[done:done + 64]):
+            i = int(t - cu[b])
+            lq, lk = int(w.lengths_q[b]), int(w.lengths_k[b])
+            vis = min(lk, max(0, i + 1 + lk - lq)) if w.causal else lk
+            flops += 4.0 * w.head_dim * w.num_heads_q * vis
+        done += len(toks)
+    el = time.perf_counter() - t0
+    return {"value": round(flops / el / 1e12, 6), "unit": "useful TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} of {w.total_q} query tokens (all {w.num_heads_q} heads), seeded random order, "
+                      f"{el:.1f} s of fp64 numpy on {threads} BLAS threads; host has "
+                      f"{len(os.sched_getaffinity(0))} usable cores"}
+
+
+def traffic_record():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it matches the kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)
+        with open(KERNEL_SOURCE, "rb") as fh:
+            sha = hashlib.sha256(fh.read()).hexdigest()
+        if rec.get("kernel_source_sha256") != sha:
+            return None
+        return int(rec["hbm_bytes_per_launch"])
+    except Exception:  # noqa: BLE001
+        return None
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-extra", action="store_true", help="skip the extra workloads")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library's hot path runs on a single device "
+              "(see the sharding notes in DESIGN.md); run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+    import varlen_flash_attention_amd as vfa
+    from varlen_flash_attention_amd.workloads import make_workload
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    vfa.load_library()
+
+    w = make_workload("long_prefill")
+    log(f"[bench] long_prefill causal: B={w.batch} lengths={w.lengths_q.tolist()} T={w.total_q}")
+    d = device_inputs(w, torch)
+    out = torch.empty((w.total_q, w.num_heads_q, w.head_dim), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w.total_q, w.num_heads_q), dtype=torch.float32, device="cuda")
+
+    def step():
+        vfa.varlen_attn_fwd(d["q"], d["k"], d["v"], d["cu_q"], d["cu_k"], w.max_seqlen_q, w.max_seqlen_k,
+                            softmax_scale=w.scale, causal=True, out=out, lse=lse)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record(stream)
+        step()
+        e.record(stream)
+        evs.append((s, e))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [s.elapsed_time(e) for s, e in evs]
+    avg_launch = sum(launch_ms) / len(launch_ms)
+    flops = w.useful_flops()
+    value = flops * args.steps / wall / 1e12
+    achieved = flops / (avg_launch * 1e-3) / 1e12
+    log(f"[bench] {args.steps} steps in {wall * 1e3:.1f} ms; avg launch {avg_launch:.3f} ms; "
+        f"{achieved:.1f} TFLOP/s useful")
+    del d, out, lse
+    torch.cuda.empty_cache()
+
+    extra = {}
+    if not args.no_extra:
+        log("[bench] extra: embed_prefill")
+        extra["embed_prefill_with_gather"] = attn_case(vfa, torch, make_workload("embed_prefill"), gather=True)
+        log("[bench] extra: long_prefill non-causal")
+        extra["long_prefill_full"] = attn_case(vfa, torch, make_workload("long_prefill_full"))
+        log("[bench] extra: decode")
+        extra["decode"] = attn_case(vfa, torch, make_workload("decode"))
+        log("[bench] extra: attn_update merge")
+        extra["attn_update_merge"] = merge_case(vfa, torch)
+
+    cpu = None
+    if not args.no_cpu:
+        log("[bench] cpu baseline (oracle)")
+        cpu = cpu_baseline(w)
+
+    result = {
+        "metric": "varlen attn useful TFLOP/s (% bf16 MFMA peak)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "long_prefill causal: 16 sequences, log-normal lengths (median 2048, sigma 1, clipped "
+                        "to [256, 8192]), TND, Hq=32 Hkv=8 D=128, bf16 in/out, fp32 accumulation, seed 3",
+            "total_tokens": w.total_q, "lengths": w.lengths_q.tolist(), "useful_gflop_per_step": round(flops / 1e9, 3),
+        },
+        "roofline": {
+            "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic_record(),
+        },
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -36,8 +36,8 @@ constexpr int kStep = 32;      // keys per wave step
 
 template <int D>
 struct DSmem {
-  static constexpr int VSTR = D * 2 + 32;                 // bytes per V row in LDS
-  static constexpr int WAVE_BYTES = 2 * kStep * VSTR;     // double-buffered steps
+  static constexpr int VSTR = D * 2 + 64;                 // bytes per V row (conflict-free tr reads)
+  static constexpr int WAVE_BYTES = kStep * VSTR;         // one step per wave (see below)
   static constexpr int VBYTES = kWaves * WAVE_BYTES;
   static constexpr int MERGE_BYTES = kWaves * kCols * (D + 2) * 4;
   static constexpr int TOTAL = VBYTES > MERGE_BYTES ? VBYTES : MERGE_BYTES;
@@ -116,24 +116,27 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decode_split_kernel(
   const int n_steps = (key_hi - key_lo + kStep - 1) / kStep;
 
   // Registers for one step: K as MFMA A operands, V rows on their way to LDS.
+  // Keys past the split end are clamped to its last key (unconditional loads:
+  // a per-lane zero-fill would force a wait on every outstanding load); the
+  // mask gives them probability 0.
   u32x4 kr[S::KREGS], vr[S::VREGS];
+  const bf16* kg = k + ((size_t)k0 * hkv + g) * D;
+  const bf16* vg = v + ((size_t)k0 * hkv + g) * D;
+  const size_t kv_stride = (size_t)hkv * D;
   auto gload = [&](int st) {
     const int base = key_lo + st * kStep;
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
       for (int ks = 0; ks < D / 32; ++ks) {
-        const int key = base + sb * 16 + c16;
-        kr[sb * (D / 32) + ks] =
-            key < key_hi ? *(const u32x4*)(k + ((size_t)(k0 + key) * hkv + g) * D + ks * 32 + grp4 * 8)
-                         : u32x4{};
+        const int key = min(base + sb * 16 + c16, key_hi - 1);
+        kr[sb * (D / 32) + ks] = *(const u32x4*)(kg + (size_t)key * kv_stride + ks * 32 + grp4 * 8);
       }
 #pragma unroll
     for (int i = 0; i < S::VREGS; ++i) {
       const int f = i * 64 + lane;
-      const int key = base + f / (D / 8);
-      const int c8 = (f % (D / 8)) * 8;
-      vr[i] = key < key_hi ? *(const u32x4*)(v + ((size_t)(k0 + key) * hkv + g) * D + c8) : u32x4{};
+      const int key = min(base + f / (D / 8), key_hi - 1);
+      vr[i] = *(const u32x4*)(vg + (size_t)key * kv_stride + (f % (D / 8)) * 8);
     }
   };
 
@@ -141,12 +144,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decode_split_kernel(
   const int tr_key = grp4 * 4 + (tr_i >> 2);
   const int tr_d = 4 * (tr_i & 3);
 
+  // A wave's LDS operations execute in issue order, so one buffer per wave is
+  // enough: the next step's writes cannot overtake this step's reads.
   int st = wave;
   if (st < n_steps) gload(st);
-  int buf = 0;
-  for (; st < n_steps; st += kWaves, buf ^= 1) {
+  for (; st < n_steps; st += kWaves) {
     // Park this step's V rows in the wave's LDS buffer, then prefetch the next step.
-    char VFA_LDS* vb = vwave + buf * kStep * S::VSTR;
+    char VFA_LDS* vb = vwave;
 #pragma unroll
     for (int i = 0; i < S::VREGS; ++i) {
       const int f = i * 64 + lane;

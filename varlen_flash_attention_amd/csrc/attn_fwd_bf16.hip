@@ -27,27 +27,39 @@
 //                   B = P^T converted to bf16 in registers.
 // K/V tiles are double-buffered in LDS; the next tile's global loads are in
 // flight while the current tile is computed.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
 namespace vfa {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * 64;
-constexpr int kCols = kWaves * 32;   // query columns per workgroup
 constexpr int kBN = 64;              // keys per tile
 
-template <int D>
+// Workgroup shapes: WAVES waves of 32 query columns each. Four waves (two
+// workgroups per CU) suit short sequences; eight waves (one workgroup per CU)
+// halve the K/V tile traffic per query column for long ones.
+template <int WAVES>
+struct Shape {
+  static constexpr int THREADS = WAVES * 64;
+  static constexpr int COLS = WAVES * 32;
+  static constexpr int MIN_BLOCKS = WAVES == 4 ? 2 : 1;
+};
+
+// LDS row strides, chosen from measured bank behaviour on gfx950: a 16-byte pad
+// makes the per-lane-row ds_read_b128 of K conflict-free; a 64-byte pad makes
+// the ds_read_b64_tr_b16 of V conflict-free (a 32-byte pad costs 2x).
+template <int D, int THREADS>
 struct Smem {
-  static constexpr int KSTR = D * 2 + 16;   // bytes per K row (16 B pad: conflict-free b128 reads)
-  static constexpr int VSTR = D * 2 + 32;   // bytes per V row (32 B pad: conflict-free tr reads)
+  static constexpr int KSTR = D * 2 + 16;
+  static constexpr int VSTR = D * 2 + 64;
   static constexpr int KBYTES = kBN * KSTR;
   static constexpr int VBYTES = kBN * VSTR;
   static constexpr int TOTAL = 2 * (KBYTES + VBYTES);
   static constexpr int CHUNKS = kBN * D / 8;          // 16-byte chunks per tile (per tensor)
-  static constexpr int PER_THREAD = CHUNKS / kThreads;
-  static_assert(CHUNKS % kThreads == 0, "tile must split evenly over the workgroup");
+  static constexpr int PER_THREAD = CHUNKS / THREADS;
+  static_assert(CHUNKS % THREADS == 0, "tile must split evenly over the workgroup");
 };
 
 __device__ __forceinline__ bf16x8 lds_read_b128(const char VFA_LDS* p) {
@@ -62,15 +74,18 @@ __device__ __forceinline__ bf16x8 lds_read_tr_pair(const char VFA_LDS* p0, const
   return __builtin_bit_cast(bf16x8, r);
 }
 
-template <int D, bool CAUSAL, typename OutT>
-__global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
+template <int WAVES, int D, bool CAUSAL, typename OutT>
+__global__ __launch_bounds__(Shape<WAVES>::THREADS, Shape<WAVES>::MIN_BLOCKS) void attn_fwd_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int batch, int hq, int hkv,
     int grp, int tokw, int n_mtiles, float scale, float scale_log2, OutT* __restrict__ out,
     float* __restrict__ lse) {
-  using S = Smem<D>;
+  constexpr int kThreads = Shape<WAVES>::THREADS;
+  using S = Smem<D, kThreads>;
   __shared__ __attribute__((aligned(16))) char smem[S::TOTAL];
   char VFA_LDS* lds = (char VFA_LDS*)smem;
+  char VFA_LDS* kbufs = lds;                      // two K tiles
+  char VFA_LDS* vbufs = lds + 2 * S::KBYTES;      // two V tiles
 
   const int per_m = batch * hkv;
   const int id = blockIdx.x;
@@ -94,8 +109,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
   const int l32 = lane & 31;
   const int half = lane >> 5;
 
-  // This lane's query column.
-  // Columns past tokw * grp (when grp does not divide kCols) carry no query.
+  // This lane's query column. Columns past tokw * grp (when grp does not
+  // divide the column count) carry no query.
   const int col = wave * 32 + l32;
   const bool colvalid = col < tokw * grp;
   const int hg = colvalid ? col / tokw : 0;
@@ -115,147 +130,171 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
     }
   }
 
-  int n_end = lk;
-  if (CAUSAL) n_end = min(lk, tok_hi + diag);
+  const int n_end = CAUSAL ? min(lk, tok_hi + diag) : lk;
   const int n_tiles = n_end > 0 ? (n_end + kBN - 1) / kBN : 0;
+  // Tiles [0, j_full) hold only keys that every row of the workgroup sees: no mask.
+  int j_full = lk / kBN;
+  if (CAUSAL) j_full = min(j_full, max(0, (tok_lo + diag + 1) / kBN));
+  j_full = min(j_full, n_tiles);
 
-  f32x16 acc[D / 32];
-#pragma unroll
-  for (int i = 0; i < D / 32; ++i) acc[i] = f32x16{};
-  float m_run = neg_inf();
-  float l_run = 0.f;
-
-  // Global -> register staging for one K/V tile.
+  // Global -> register staging; K runs one tile ahead of V.
   u32x4 kst[S::PER_THREAD], vst[S::PER_THREAD];
-  auto gload = [&](int tile) {
+  const int st_key = tid / (D / 8);              // key of chunk i is st_key + i * (kThreads / (D / 8))
+  const int st_c8 = (tid % (D / 8)) * 8;
+  constexpr int KEYS_PER_PASS = kThreads / (D / 8);
+  const bf16* kbase = k + ((size_t)k0 * hkv + g) * D + st_c8;
+  const bf16* vbase = v + ((size_t)k0 * hkv + g) * D + st_c8;
+  const size_t kv_stride = (size_t)hkv * D;
+  // Rows past the sequence end are clamped to its last key instead of being
+  // skipped: the loads stay unconditional (a per-lane branch that zero-fills
+  // the destination forces a wait on every outstanding load), and those keys
+  // are masked to probability 0 anyway.
+  auto gload = [&](u32x4 (&dst)[S::PER_THREAD], const bf16* base, int tile) {
 #pragma unroll
     for (int i = 0; i < S::PER_THREAD; ++i) {
-      const int f = i * kThreads + tid;
-      const int key = f / (D / 8);
-      const int c8 = (f % (D / 8)) * 8;
-      const int kk = tile * kBN + key;
-      if (kk < lk) {
-        const size_t off = ((size_t)(k0 + kk) * hkv + g) * D + c8;
-        kst[i] = *(const u32x4*)(k + off);
-        vst[i] = *(const u32x4*)(v + off);
-      } else {
-        kst[i] = u32x4{};
-        vst[i] = u32x4{};
-      }
+      const int kk = min(tile * kBN + st_key + i * KEYS_PER_PASS, lk - 1);
+      dst[i] = *(const u32x4*)(base + (size_t)kk * kv_stride);
     }
   };
-  auto sstore = [&](int buf) {
-    char VFA_LDS* kb = lds + buf * S::KBYTES;
-    char VFA_LDS* vb = lds + 2 * S::KBYTES + buf * S::VBYTES;
+  auto sstore = [&](const u32x4 (&src)[S::PER_THREAD], char VFA_LDS* buf, int stride) {
 #pragma unroll
-    for (int i = 0; i < S::PER_THREAD; ++i) {
-      const int f = i * kThreads + tid;
-      const int key = f / (D / 8);
-      const int c8 = (f % (D / 8)) * 8;
-      *(u32x4 VFA_LDS*)(kb + key * S::KSTR + c8 * 2) = kst[i];
-      *(u32x4 VFA_LDS*)(vb + key * S::VSTR + c8 * 2) = vst[i];
-    }
+    for (int i = 0; i < S::PER_THREAD; ++i)
+      *(u32x4 VFA_LDS*)(buf + (st_key + i * KEYS_PER_PASS) * stride + st_c8 * 2) = src[i];
   };
 
-  if (n_tiles > 0) {
-    gload(0);
-    sstore(0);
-  }
-  __syncthreads();
-
-  // Lane geometry of the transposed V reads (see ds_read_b64_tr_b16): in each
-  // 16-lane group, lane i receives d = dbase + i for 4 consecutive keys.
-  const int tr_grp = lane >> 4;
-  const int tr_i = lane & 15;
-  const int tr_key = (tr_grp >> 1) * 4 + (tr_i >> 2);
-  const int tr_d = (tr_grp & 1) * 16 + 4 * (tr_i & 3);
-
-  for (int j = 0; j < n_tiles; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < n_tiles) gload(j + 1);
-
-    const char VFA_LDS* kb = lds + buf * S::KBYTES;
-    const char VFA_LDS* vb = lds + 2 * S::KBYTES + buf * S::VBYTES;
-
-    // S^T for two 32-key sub-blocks: rows = keys, column = this lane's query.
-    f32x16 s[2];
+  // S^T for one 64-key tile: two 32-key sub-blocks, rows = keys, column = this lane's query.
+  auto qk = [&](const char VFA_LDS* kb, f32x16 (&s)[2]) {
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
       s[sb] = f32x16{};
       const char VFA_LDS* krow = kb + (sb * 32 + l32) * S::KSTR + half * 16;
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        bf16x8 a = lds_read_b128(krow + ks * 32);
-        s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], s[sb], 0, 0, 0);
-      }
+      for (int ks = 0; ks < D / 16; ++ks)
+        s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read_b128(krow + ks * 32), qreg[ks], s[sb], 0, 0, 0);
     }
+  };
 
-    // Mask only the tiles that cross the sequence end or the causal diagonal.
-    const int tile_k0 = j * kBN;
-    const bool need_mask = (tile_k0 + kBN > lk) || (CAUSAL && tile_k0 + kBN - 1 > tok_lo + diag);
-    if (need_mask) {
+  // Transposed V reads (ds_read_b64_tr_b16): in each 16-lane group, lane i
+  // receives d = dbase + i for 4 consecutive keys.
+  const int tr_grp = lane >> 4;
+  const int tr_i = lane & 15;
+  const int tr_key = (tr_grp >> 1) * 4 + (tr_i >> 2);
+  const int tr_d = (tr_grp & 1) * 16 + 4 * (tr_i & 3);
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) acc[i] = f32x16{};
+  // Running reference max (raw score units) and running sum. The reference is
+  // only moved when some column's tile max exceeds it by more than 2^8 in
+  // probability terms, so most tiles skip the rescale of O.
+  float m_run = neg_inf();
+  float l_run = 0.f;
+  const float tau = 8.f / scale_log2;
+
+  auto softmax_pv = [&](auto masked, f32x16 (&s)[2], int j) {
+    if constexpr (decltype(masked)::value) {
       const int lim = CAUSAL ? min(lk - 1, tq + diag) : lk - 1;
+      const int kb0 = j * kBN + half * 4;
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = tile_k0 + sb * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
-          if (key > lim) s[sb][r] = neg_inf();
-        }
+        for (int r = 0; r < 16; ++r)
+          if (kb0 + sb * 32 + (r >> 2) * 8 + (r & 3) > lim) s[sb][r] = neg_inf();
     }
-
-    // Online softmax (base 2, scale folded into one FMA).
-    float mx = neg_inf();
+    float lm = neg_inf();
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sb][r]);
-    mx = fmaxf(mx, xor_shuffle(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == neg_inf()) ? 0.f : m_new;
-    const float alpha = fast_exp2((m_run - m_use) * scale_log2);
-    const float ms = m_use * scale_log2;
-    m_run = m_new;
-
+      for (int r = 0; r < 16; ++r) lm = fmaxf(lm, s[sb][r]);
+    // The other lane half holds the other keys of the same column.
+    {
+      auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lm), __float_as_uint(lm), false, false);
+      lm = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
+    // Probabilities against the current reference (speculative: redone below if it moves).
     bf16x8 p[4];
-    float psum = 0.f;
+    float ts = 0.f;
+    auto make_p = [&](float mref) {
+      ts = 0.f;
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
+      for (int x = 0; x < 4; ++x) {
+        const int sb = x >> 1, hh = x & 1;
+        bf16x2 pr[4];
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        float e[8];
-#pragma unroll
-        for (int x = 0; x < 8; ++x) {
-          e[x] = fast_exp2(__builtin_fmaf(s[sb][hh * 8 + x], scale_log2, -ms));
-          psum += e[x];
+        for (int y = 0; y < 4; ++y) {
+          const float e0 = fast_exp2(__builtin_fmaf(s[sb][hh * 8 + 2 * y], scale_log2, -mref));
+          const float e1 = fast_exp2(__builtin_fmaf(s[sb][hh * 8 + 2 * y + 1], scale_log2, -mref));
+          pr[y] = f32x2_to_bf16x2(e0, e1);
+          ts += e0 + e1;   // fp32 sum of the unrounded probabilities: lse stays fp32-accurate
         }
-        bf16x2 p01 = f32x2_to_bf16x2(e[0], e[1]);
-        bf16x2 p23 = f32x2_to_bf16x2(e[2], e[3]);
-        bf16x2 p45 = f32x2_to_bf16x2(e[4], e[5]);
-        bf16x2 p67 = f32x2_to_bf16x2(e[6], e[7]);
-        p[sb * 2 + hh] = bf16x8{p01[0], p01[1], p23[0], p23[1], p45[0], p45[1], p67[0], p67[1]};
+        p[x] = bf16x8{pr[0][0], pr[0][1], pr[1][0], pr[1][1], pr[2][0], pr[2][1], pr[3][0], pr[3][1]};
       }
-    l_run = l_run * alpha + psum;
-
+    };
+    make_p(m_run == neg_inf() ? 0.f : m_run * scale_log2);
+    const bool need = lm > m_run + tau;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      const float m_new = need ? lm : m_run;
+      // Lanes that keep their reference scale by exactly 1 (their m_run may be -inf);
+      // a reference moving up from -inf scales the (zero) history by 0.
+      const float alpha = need ? fast_exp2((m_run - m_new) * scale_log2) : 1.f;
+      m_run = m_new;
+      l_run *= alpha;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+      for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+      make_p(m_run == neg_inf() ? 0.f : m_run * scale_log2);
+    }
+    l_run += ts;
 
     // O^T += V^T P^T over four 16-key steps.
+    const char VFA_LDS* vb = vbufs + (j & 1) * S::VBYTES;
 #pragma unroll
     for (int kstep = 0; kstep < 4; ++kstep) {
-      const char VFA_LDS* vbase = vb + (kstep * 16 + tr_key) * S::VSTR + tr_d * 2;
+      const char VFA_LDS* vrow = vb + (kstep * 16 + tr_key) * S::VSTR + tr_d * 2;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
-        bf16x8 a = lds_read_tr_pair(vbase + db * 64, vbase + 8 * S::VSTR + db * 64);
+        bf16x8 a = lds_read_tr_pair(vrow + db * 64, vrow + 8 * S::VSTR + db * 64);
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p[kstep], acc[db], 0, 0, 0);
       }
     }
+  };
 
-    if (j + 1 < n_tiles) sstore(buf ^ 1);
-    __syncthreads();
+  // Prologue: K(0), V(0), K(1) in LDS; K(2), V(1) in registers; S = QK(0).
+  if (n_tiles > 0) {
+    gload(kst, kbase, 0);
+    gload(vst, vbase, 0);
+    sstore(kst, kbufs, S::KSTR);
+    sstore(vst, vbufs, S::VSTR);
+    if (n_tiles > 1) {
+      gload(kst, kbase, 1);
+      sstore(kst, kbufs + S::KBYTES, S::KSTR);
+    }
   }
+  __syncthreads();
+  if (n_tiles > 2) gload(kst, kbase, 2);
+  if (n_tiles > 1) gload(vst, vbase, 1);
+  f32x16 s_cur[2];
+  qk(kbufs, s_cur);
+
+  auto tile_step = [&](auto masked, int j) {
+    // Everyone is done with QK(j) and PV(j-1): K buffer j%2 and V buffer (j+1)%2
+    // are free, and K(j+1), V(j) (stored last iteration) are visible.
+    __syncthreads();
+    if (j + 2 < n_tiles) sstore(kst, kbufs + (j & 1) * S::KBYTES, S::KSTR);
+    if (j + 1 < n_tiles) sstore(vst, vbufs + ((j + 1) & 1) * S::VBYTES, S::VSTR);
+    if (j + 3 < n_tiles) gload(kst, kbase, j + 3);
+    if (j + 2 < n_tiles) gload(vst, vbase, j + 2);
+    // QK of the next tile (harmless garbage after the last tile) overlaps this tile's softmax.
+    f32x16 s_next[2];
+    qk(kbufs + ((j + 1) & 1) * S::KBYTES, s_next);
+    softmax_pv(masked, s_cur, j);
+    s_cur[0] = s_next[0];
+    s_cur[1] = s_next[1];
+  };
+  int j = 0;
+  for (; j < j_full; ++j) tile_step(std::integral_constant<bool, false>{}, j);
+  for (; j < n_tiles; ++j) tile_step(std::integral_constant<bool, true>{}, j);
 
   // Epilogue: combine the two lane halves' partial sums, normalise, store.
   const float l_tot = l_run + xor_shuffle(l_run, 32);
@@ -282,30 +321,39 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
   }
 }
 
-template <int D, bool CAUSAL, typename OutT>
+template <int WAVES, int D, bool CAUSAL, typename OutT>
 int launch_t(const AttnArgs& a) {
-  const int tokw = kCols / a.grp;
+  const int tokw = Shape<WAVES>::COLS / a.grp;
   const int n_mtiles = (a.max_seqlen_q + tokw - 1) / tokw;
   const long long blocks = (long long)n_mtiles * a.batch * a.hkv;
   if (blocks <= 0) return 0;
   if (blocks > 0x7fffffffLL) return -1;
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, OutT>), dim3((unsigned)blocks), dim3(kThreads), 0,
-                     (hipStream_t)a.stream, (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.cu_q,
-                     a.cu_k, a.batch, a.hq, a.hkv, a.grp, tokw, n_mtiles, a.scale, a.scale * kLog2e,
-                     (OutT*)a.out, a.lse);
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<WAVES, D, CAUSAL, OutT>), dim3((unsigned)blocks),
+                     dim3(Shape<WAVES>::THREADS), 0, (hipStream_t)a.stream, (const bf16*)a.q, (const bf16*)a.k,
+                     (const bf16*)a.v, a.cu_q, a.cu_k, a.batch, a.hq, a.hkv, a.grp, tokw, n_mtiles, a.scale,
+                     a.scale * kLog2e, (OutT*)a.out, a.lse);
   return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+template <int WAVES>
+int launch_w(const AttnArgs& a) {
+  const bool f32out = a.out_dtype == 0;
+  if (a.head_dim == 128) {
+    if (a.causal) return f32out ? launch_t<WAVES, 128, true, float>(a) : launch_t<WAVES, 128, true, bf16>(a);
+    return f32out ? launch_t<WAVES, 128, false, float>(a) : launch_t<WAVES, 128, false, bf16>(a);
+  }
+  if (a.causal) return f32out ? launch_t<WAVES, 64, true, float>(a) : launch_t<WAVES, 64, true, bf16>(a);
+  return f32out ? launch_t<WAVES, 64, false, float>(a) : launch_t<WAVES, 64, false, bf16>(a);
 }
 
 }  // namespace
 
+// Eight-wave workgroups once sequences average at least eight of their
+// query tiles (256 / G tokens); shorter ones waste less with four waves.
 int launch_attn_fwd_bf16(const AttnArgs& a) {
-  const bool f32out = a.out_dtype == 0;
-  if (a.head_dim == 128) {
-    if (a.causal) return f32out ? launch_t<128, true, float>(a) : launch_t<128, true, bf16>(a);
-    return f32out ? launch_t<128, false, float>(a) : launch_t<128, false, bf16>(a);
-  }
-  if (a.causal) return f32out ? launch_t<64, true, float>(a) : launch_t<64, true, bf16>(a);
-  return f32out ? launch_t<64, false, float>(a) : launch_t<64, false, bf16>(a);
+  const long long mean_q = a.batch > 0 ? (long long)a.total_q / a.batch : 0;
+  if (mean_q >= 8LL * (Shape<8>::COLS / a.grp)) return launch_w<8>(a);
+  return launch_w<4>(a);
 }
 
 }  // namespace vfa
