@@ -193,6 +193,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the extra workloads")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed region, copy 256 MiB device-to-device with cold caches: a kernel of "
+                         "known traffic against which rocprofv3 FETCH_SIZE / WRITE_SIZE readings are scaled")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library's hot path runs on a single device "
@@ -241,6 +244,16 @@ def main() -> int:
         f"{achieved:.1f} TFLOP/s useful")
     del d, out, lse
     torch.cuda.empty_cache()
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.uint8, device="cuda").fill_(7)
+        dst = torch.empty_like(src)
+        scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)   # evict src from L2 / MALL
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] copy calibration: 268435456 bytes read, 268435456 bytes written")
+        del src, dst, scratch
+        torch.cuda.empty_cache()
 
     extra = {}
     if not args.no_extra:

@@ -36,6 +36,7 @@ namespace vfa {
 namespace {
 
 constexpr int kBN = 64;              // keys per tile
+constexpr int kXcds = 8;             // MI355X: 8 XCDs, blocks dispatched round-robin
 
 // Workgroup shapes: WAVES waves of 32 query columns each. Four waves (two
 // workgroups per CU) suit short sequences; eight waves (one workgroup per CU)
@@ -87,10 +88,18 @@ __global__ __launch_bounds__(Shape<WAVES>::THREADS, Shape<WAVES>::MIN_BLOCKS) vo
   char VFA_LDS* kbufs = lds;                      // two K tiles
   char VFA_LDS* vbufs = lds + 2 * S::KBYTES;      // two V tiles
 
+  // Block -> work. Consecutive block ids go round-robin to the 8 XCDs, each
+  // with its own L2. XCD x takes the (sequence, kv head) pairs x, x + 8, ...
+  // one after another, and for each pair all of its query tiles back to back
+  // (last tile first: causal rows grow with the tile index), so the blocks
+  // resident on an XCD at one time mostly share one pair's K/V in L2.
   const int per_m = batch * hkv;
   const int id = blockIdx.x;
-  const int m = n_mtiles - 1 - id / per_m;
-  const int bg = id % per_m;
+  const int xcd = id % kXcds;
+  const int slot = id / kXcds;
+  const int bg = (slot / n_mtiles) * kXcds + xcd;
+  if (bg >= per_m) return;
+  const int m = n_mtiles - 1 - slot % n_mtiles;
   const int b = bg / hkv;
   const int g = bg % hkv;
 
@@ -325,7 +334,8 @@ template <int WAVES, int D, bool CAUSAL, typename OutT>
 int launch_t(const AttnArgs& a) {
   const int tokw = Shape<WAVES>::COLS / a.grp;
   const int n_mtiles = (a.max_seqlen_q + tokw - 1) / tokw;
-  const long long blocks = (long long)n_mtiles * a.batch * a.hkv;
+  const long long pairs_per_xcd = ((long long)a.batch * a.hkv + kXcds - 1) / kXcds;
+  const long long blocks = (long long)n_mtiles * pairs_per_xcd * kXcds;
   if (blocks <= 0) return 0;
   if (blocks > 0x7fffffffLL) return -1;
   hipLaunchKernelGGL((attn_fwd_bf16_kernel<WAVES, D, CAUSAL, OutT>), dim3((unsigned)blocks),
