@@ -92,7 +92,9 @@ size_t varlen_attn_fwd_workspace_size(int32_t batch, int32_t total_q,
  *         lengths; they size the launch so that no device-to-host copy of
  *         cu_seqlens is needed ([P1] core optimisation 1 keeps cu_seqlens
  *         on the host for the same reason). A bound below a real length
- *         leaves that sequence's excess rows unwritten.
+ *         is a caller error: that sequence's excess query rows are left
+ *         unwritten and, on the split-KV (decode) path, its keys past the
+ *         bound are ignored; nothing is read or written out of bounds.
  * out     [total_q, num_heads_q, head_dim]    out_dtype
  * lse     [total_q, num_heads_q]              fp32
  * workspace / workspace_bytes: device scratch of at least
@@ -126,7 +128,9 @@ int32_t varlen_attn_fwd(const void* q, const void* k, const void* v, int32_t in_
  *                          then it must not be NULL; ignored when 0.
  * Row order is free to the caller; varlen_attn_fwd's partials use
  * r = token * num_heads_q + head, so its out/lse feed this call directly.
- * Supported: hd in {64, 128}, 1 <= sp <= 64. bsh == 0 returns VFA_OK.
+ * Supported: hd in {64, 128}, any sp >= 1 (sp <= 16 keeps every partial's
+ * load in flight at once; larger sp streams). go and out 16-byte aligned.
+ * bsh == 0 returns VFA_OK.
  */
 int32_t attn_update(const float* lse, const void* go, int32_t go_dtype,
                     int32_t sp, int64_t bsh, int32_t hd, int32_t update_type,

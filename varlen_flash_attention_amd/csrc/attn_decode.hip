@@ -272,7 +272,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decode_split_kernel(
 template <int D, typename OutT>
 __global__ __launch_bounds__(256) void attn_decode_combine_kernel(
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int batch, int hq, int chunk,
-    long long rows_total, const float* __restrict__ ws_o, const float* __restrict__ ws_lse,
+    int n_splits, long long rows_total, const float* __restrict__ ws_o, const float* __restrict__ ws_lse,
     OutT* __restrict__ out, float* __restrict__ lse) {
   constexpr int TPR = D / 4;
   constexpr int RPB = 256 / TPR;
@@ -287,7 +287,9 @@ __global__ __launch_bounds__(256) void attn_decode_combine_kernel(
     if (cu_q[mid] <= tok) lo = mid; else hi = mid;
   }
   const int lk = cu_k[lo + 1] - cu_k[lo];
-  const int n = lk > 0 ? (lk + chunk - 1) / chunk : 0;
+  // Splits written for this sequence (keys past a too-small max_seqlen_k bound
+  // were never split: the count is capped at the workspace's split count).
+  const int n = lk > 0 ? min((lk + chunk - 1) / chunk, n_splits) : 0;
   const MergeStats st = merge_stats(ws_lse + row, rows_total, n);
   f32x4 o = f32x4{};
   for (int s = 0; s < n; ++s) {
@@ -317,7 +319,7 @@ int launch_t(const AttnArgs& a, const DecodePlan& p) {
   constexpr int RPB = 256 / (D / 4);
   const long long cblocks = (rows + RPB - 1) / RPB;
   hipLaunchKernelGGL((attn_decode_combine_kernel<D, OutT>), dim3((unsigned)cblocks), dim3(256), 0,
-                     (hipStream_t)a.stream, a.cu_q, a.cu_k, a.batch, a.hq, p.chunk, rows, ws_o, ws_lse,
+                     (hipStream_t)a.stream, a.cu_q, a.cu_k, a.batch, a.hq, p.chunk, p.n_splits, rows, ws_o, ws_lse,
                      (OutT*)a.out, a.lse);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
