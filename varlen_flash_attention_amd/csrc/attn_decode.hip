@@ -37,11 +37,12 @@ constexpr int kStep = 32;      // keys per wave step
 template <int D>
 struct DSmem {
   static constexpr int VSTR = D * 2 + 64;                 // bytes per V row (conflict-free tr reads)
-  static constexpr int WAVE_BYTES = kStep * VSTR;         // one step per wave (see below)
+  static constexpr int KSTR = D * 2 + 16;                 // bytes per K row (conflict-free b128 reads)
+  static constexpr int WAVE_BYTES = kStep * (VSTR + KSTR); // one step of K and V per wave (see below)
   static constexpr int VBYTES = kWaves * WAVE_BYTES;
   static constexpr int MERGE_BYTES = kWaves * kCols * (D + 2) * 4;
   static constexpr int TOTAL = VBYTES > MERGE_BYTES ? VBYTES : MERGE_BYTES;
-  static constexpr int KREGS = 2 * (D / 32);               // 16-byte K loads per lane per step
+  static constexpr int KREGS = kStep * D / 8 / 64;         // 16-byte K loads per lane per step
   static constexpr int VREGS = kStep * D / 8 / 64;         // 16-byte V loads per lane per step
 };
 
@@ -112,64 +113,61 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decode_split_kernel(
   float m_run = neg_inf();
   float l_run = 0.f;
 
-  char VFA_LDS* vwave = lds + wave * S::WAVE_BYTES;
   const int n_steps = (key_hi - key_lo + kStep - 1) / kStep;
 
   // Registers for one step: K as MFMA A operands, V rows on their way to LDS.
   // Keys past the split end are clamped to its last key (unconditional loads:
   // a per-lane zero-fill would force a wait on every outstanding load); the
-  // mask gives them probability 0.
-  u32x4 kr[S::KREGS], vr[S::VREGS];
+  // mask gives them probability 0. Two register sets keep two steps of loads
+  // in flight per wave while a third is computed.
+  typedef u32x4 KRegs[S::KREGS];
+  typedef u32x4 VRegs[S::VREGS];
+  KRegs kA, kB;
+  VRegs vA, vB;
   const bf16* kg = k + ((size_t)k0 * hkv + g) * D;
   const bf16* vg = v + ((size_t)k0 * hkv + g) * D;
   const size_t kv_stride = (size_t)hkv * D;
-  auto gload = [&](int st) {
+  // K and V rows are loaded whole (each instruction covers 64 / (D/8) rows of
+  // contiguous bytes) and parked in the wave's LDS buffers.
+  auto gload = [&](KRegs& kr, VRegs& vr, int st) {
     const int base = key_lo + st * kStep;
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks) {
-        const int key = min(base + sb * 16 + c16, key_hi - 1);
-        kr[sb * (D / 32) + ks] = *(const u32x4*)(kg + (size_t)key * kv_stride + ks * 32 + grp4 * 8);
-      }
 #pragma unroll
     for (int i = 0; i < S::VREGS; ++i) {
       const int f = i * 64 + lane;
       const int key = min(base + f / (D / 8), key_hi - 1);
-      vr[i] = *(const u32x4*)(vg + (size_t)key * kv_stride + (f % (D / 8)) * 8);
+      const size_t off = (size_t)key * kv_stride + (f % (D / 8)) * 8;
+      kr[i] = *(const u32x4*)(kg + off);
+      vr[i] = *(const u32x4*)(vg + off);
     }
   };
 
   const int tr_i = lane & 15;
   const int tr_key = grp4 * 4 + (tr_i >> 2);
   const int tr_d = 4 * (tr_i & 3);
-
-  // A wave's LDS operations execute in issue order, so one buffer per wave is
+  // A wave's LDS operations execute in issue order, so one V buffer per wave is
   // enough: the next step's writes cannot overtake this step's reads.
-  int st = wave;
-  if (st < n_steps) gload(st);
-  for (; st < n_steps; st += kWaves) {
-    // Park this step's V rows in the wave's LDS buffer, then prefetch the next step.
-    char VFA_LDS* vb = vwave;
+  char VFA_LDS* vb = lds + wave * S::WAVE_BYTES;
+  char VFA_LDS* kbw = vb + kStep * S::VSTR;
+
+  auto step = [&](const KRegs& kr, const VRegs& vr, int st) {
 #pragma unroll
     for (int i = 0; i < S::VREGS; ++i) {
       const int f = i * 64 + lane;
       *(u32x4 VFA_LDS*)(vb + (f / (D / 8)) * S::VSTR + (f % (D / 8)) * 16) = vr[i];
+      *(u32x4 VFA_LDS*)(kbw + (f / (D / 8)) * S::KSTR + (f % (D / 8)) * 16) = kr[i];
     }
-    u32x4 kcur[S::KREGS];
-#pragma unroll
-    for (int i = 0; i < S::KREGS; ++i) kcur[i] = kr[i];
-    if (st + kWaves < n_steps) gload(st + kWaves);
-
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     // S^T for two 16-key blocks: lane holds keys sb*16 + grp4*4 + r of column c16.
+    // A operand: row = key sb*16 + c16, k-slot grp4*8 + e <-> d = ks*32 + grp4*8 + e.
     f32x4 s[2];
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
       s[sb] = f32x4{};
+      const char VFA_LDS* krow = kbw + (sb * 16 + c16) * S::KSTR + grp4 * 16;
 #pragma unroll
       for (int ks = 0; ks < D / 32; ++ks)
-        s[sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kcur[sb * (D / 32) + ks]),
-                                                        qreg[ks], s[sb], 0, 0, 0);
+        s[sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8 VFA_LDS*)(krow + ks * 64), qreg[ks], s[sb],
+                                                        0, 0, 0);
     }
 
     const int base = key_lo + st * kStep;
@@ -227,6 +225,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decode_split_kernel(
       acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, p, acc[db], 0, 0, 0);
     }
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  };
+
+  // This wave's steps are wave, wave + 4, ...; sets A and B alternate.
+  int st = wave;
+  if (st < n_steps) gload(kA, vA, st);
+  if (st + kWaves < n_steps) gload(kB, vB, st + kWaves);
+  for (; st < n_steps; st += 2 * kWaves) {
+    step(kA, vA, st);
+    if (st + 2 * kWaves < n_steps) gload(kA, vA, st + 2 * kWaves);
+    if (st + kWaves < n_steps) {
+      step(kB, vB, st + kWaves);
+      if (st + 3 * kWaves < n_steps) gload(kB, vB, st + 3 * kWaves);
+    }
   }
 
   // Per-wave totals: the four lanes of a column hold disjoint keys.
@@ -268,40 +279,79 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decode_split_kernel(
   if ((tid & 15) == 0) ws_lse[(long long)split * rows_total + row] = lse_m;
 }
 
-// Merge the splits of every row: one row per TPR threads, 16-byte loads.
-template <int D, typename OutT>
+// Merge the splits of every row with the AttentionUpdate rule. Grid: (row
+// chunk, sequence); one row per TPR lanes with 16-byte loads. NS is a
+// compile-time bound on the split count so that every lse and partial load of
+// a row is issued before the first one is consumed (NS = 0: streaming loop
+// for very long key sets).
+template <int D, int NS, typename OutT>
 __global__ __launch_bounds__(256) void attn_decode_combine_kernel(
-    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int batch, int hq, int chunk,
-    int n_splits, long long rows_total, const float* __restrict__ ws_o, const float* __restrict__ ws_lse,
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int hq, int chunk, int n_splits,
+    long long rows_total, const float* __restrict__ ws_o, const float* __restrict__ ws_lse,
     OutT* __restrict__ out, float* __restrict__ lse) {
   constexpr int TPR = D / 4;
   constexpr int RPB = 256 / TPR;
-  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / TPR;
-  if (row >= rows_total) return;
+  const int b = blockIdx.y;
+  const int q0 = cu_q[b];
+  const int rows_b = (cu_q[b + 1] - q0) * hq;
+  const int r_in = blockIdx.x * RPB + threadIdx.x / TPR;
+  if (r_in >= rows_b) return;
+  const long long row = (long long)q0 * hq + r_in;
   const int c4 = (threadIdx.x % TPR) * 4;
-  const int tok = (int)(row / hq);
-  // Sequence of this token: largest b with cu_q[b] <= tok.
-  int lo = 0, hi = batch;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (cu_q[mid] <= tok) lo = mid; else hi = mid;
-  }
-  const int lk = cu_k[lo + 1] - cu_k[lo];
+  const int lk = cu_k[b + 1] - cu_k[b];
   // Splits written for this sequence (keys past a too-small max_seqlen_k bound
   // were never split: the count is capped at the workspace's split count).
   const int n = lk > 0 ? min((lk + chunk - 1) / chunk, n_splits) : 0;
-  const MergeStats st = merge_stats(ws_lse + row, rows_total, n);
   f32x4 o = f32x4{};
-  for (int s = 0; s < n; ++s) {
-    const float w = merge_weight(ws_lse[(long long)s * rows_total + row], st);
-    const f32x4 x = *(const f32x4*)(ws_o + ((long long)s * rows_total + row) * D + c4);
+  float lse_m;
+  if constexpr (NS > 0) {
+    float l[NS], w[NS];
 #pragma unroll
-    for (int y = 0; y < 4; ++y) o[y] += w * x[y];
+    for (int i = 0; i < NS; ++i) l[i] = i < n ? ws_lse[(long long)i * rows_total + row] : neg_inf();
+    lse_m = merge_weights<NS>(l, n, w);
+#pragma unroll
+    for (int i0 = 0; i0 < NS; i0 += 8) {
+      f32x4 x[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        x[i] = i0 + i < n ? *(const f32x4*)(ws_o + ((long long)(i0 + i) * rows_total + row) * D + c4) : f32x4{};
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int y = 0; y < 4; ++y) o[y] += w[i0 + i] * x[i][y];
+    }
+  } else {
+    const MergeStats st = merge_stats(ws_lse + row, rows_total, n);
+    for (int s = 0; s < n; ++s) {
+      const float w = merge_weight(ws_lse[(long long)s * rows_total + row], st);
+      const f32x4 x = *(const f32x4*)(ws_o + ((long long)s * rows_total + row) * D + c4);
+#pragma unroll
+      for (int y = 0; y < 4; ++y) o[y] += w * x[y];
+    }
+    lse_m = st.lse_m;
   }
   OutT* dst = out + row * D + c4;
 #pragma unroll
   for (int y = 0; y < 4; ++y) dst[y] = from_f32<OutT>(o[y]);
-  if (c4 == 0) lse[row] = st.lse_m;
+  if (c4 == 0) lse[row] = lse_m;
+}
+
+template <int D, typename OutT>
+void launch_combine(const AttnArgs& a, const DecodePlan& p, long long rows, const float* ws_o,
+                    const float* ws_lse) {
+  constexpr int RPB = 256 / (D / 4);
+  const long long max_rows = (long long)a.max_seqlen_q * a.hq;
+  const dim3 grid((unsigned)((max_rows + RPB - 1) / RPB), (unsigned)a.batch);
+  hipStream_t st = (hipStream_t)a.stream;
+#define VFA_COMBINE(NS)                                                                                    \
+  hipLaunchKernelGGL((attn_decode_combine_kernel<D, NS, OutT>), grid, dim3(256), 0, st, a.cu_q, a.cu_k, a.hq, \
+                     p.chunk, p.n_splits, rows, ws_o, ws_lse, (OutT*)a.out, a.lse)
+  if (p.n_splits <= 8) VFA_COMBINE(8);
+  else if (p.n_splits <= 16) VFA_COMBINE(16);
+  else if (p.n_splits <= 32) VFA_COMBINE(32);
+  else if (p.n_splits <= 64) VFA_COMBINE(64);
+  else VFA_COMBINE(0);
+#undef VFA_COMBINE
 }
 
 template <int D, bool CAUSAL, typename OutT>
@@ -316,11 +366,7 @@ int launch_t(const AttnArgs& a, const DecodePlan& p) {
                      a.cu_k, a.batch, a.hq, a.hkv, a.grp, p.chunk, p.n_splits, rows, a.scale,
                      a.scale * kLog2e, ws_o, ws_lse);
   if (hipGetLastError() != hipSuccess) return -1;
-  constexpr int RPB = 256 / (D / 4);
-  const long long cblocks = (rows + RPB - 1) / RPB;
-  hipLaunchKernelGGL((attn_decode_combine_kernel<D, OutT>), dim3((unsigned)cblocks), dim3(256), 0,
-                     (hipStream_t)a.stream, a.cu_q, a.cu_k, a.batch, a.hq, p.chunk, p.n_splits, rows, ws_o, ws_lse,
-                     (OutT*)a.out, a.lse);
+  launch_combine<D, OutT>(a, p, rows, ws_o, ws_lse);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
