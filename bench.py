@@ -53,11 +53,17 @@ def device_inputs(w, torch):
                 cu_k=torch.from_numpy(w.cu_seqlens_k).cuda())
 
 
-def time_calls(fn, reps, warmup, torch, flush=None):
-    """Per-call durations (ms) from HIP events on the current stream."""
+def time_calls(fn, reps, warmup, torch, flush=None, queue_ahead=False):
+    """Per-call durations (ms) from HIP events on the current stream.
+
+    queue_ahead: hold the stream in a spin kernel while the host enqueues every
+    call, so that a kernel shorter than its own host launch cost is timed back
+    to back rather than as launch-bound gaps."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
+    if queue_ahead:
+        torch.cuda._sleep(int(2.0e5 * reps))      # ~0.1 ms per queued call at 2 GHz
     ev = []
     for _ in range(reps):
         if flush is not None:
@@ -128,15 +134,36 @@ def merge_case(vfa, torch, reps=100, warmup=5):
         vfa.attn_update(lse, go, 1, out=out, lse_out=lse_out)
 
     cold = time_calls(call, reps, warmup, torch, flush=flush)
-    warm = time_calls(call, reps, warmup, torch)
+    warm = time_calls(call, reps, warmup, torch, queue_ahead=True)
+    # Floor for moving this many bytes at all: a device-to-device copy of half
+    # of them (read + write = algo_bytes), cold, timed the same way.
+    csrc = torch.empty(algo_bytes // 2, dtype=torch.uint8, device="cuda").fill_(7)
+    cdst = torch.empty_like(csrc)
+    copy_cold = time_calls(lambda: cdst.copy_(csrc), reps, warmup, torch, flush=flush)
     res = {}
-    for name, ms in (("cold", cold), ("warm", warm)):
+    for name, ms in (("cold", cold), ("warm", warm), ("copy_floor_cold", copy_cold)):
         t = median(ms)
         res[name] = {"us_median": round(t * 1e3, 3), "gb_per_s": round(algo_bytes / t / 1e6, 1),
                      "frac_hbm_peak": round(algo_bytes / t / 1e6 / PEAK_HBM_GBPS, 4)}
     res["algorithmic_bytes"] = algo_bytes
     res["shape"] = {"sp": sp, "bsh": bsh, "hd": hd, "dtype": "fp32"}
-    del scratch
+    del scratch, csrc, cdst, go, out, lse, lse_out
+    torch.cuda.empty_cache()
+
+    # The same kernel on 32x the rows (302 MB, larger than the last-level
+    # cache): what it sustains once launch and first-byte latency amortise.
+    big = 32 * bsh
+    lse = torch.randn((sp, big), dtype=torch.float32, device="cuda")
+    go = torch.randn((sp, big, hd), dtype=torch.float32, device="cuda")
+    out = torch.empty((big, hd), dtype=torch.float32, device="cuda")
+    lse_out = torch.empty((big,), dtype=torch.float32, device="cuda")
+    big_bytes = sp * big * (hd + 1) * 4 + big * (hd + 1) * 4
+    ms = time_calls(lambda: vfa.attn_update(lse, go, 1, out=out, lse_out=lse_out), 20, 3, torch)
+    t = median(ms)
+    res["rows_x32"] = {"us_median": round(t * 1e3, 3), "gb_per_s": round(big_bytes / t / 1e6, 1),
+                       "frac_hbm_peak": round(big_bytes / t / 1e6 / PEAK_HBM_GBPS, 4),
+                       "algorithmic_bytes": big_bytes, "bsh": big}
+    del lse, go, out, lse_out
     torch.cuda.empty_cache()
     return res
 

@@ -164,15 +164,29 @@ attn_fwd_bf16_kernel(
   const int st_key = tid / (D / 8);
   const int st_c8 = (tid % (D / 8)) * 8;
   constexpr int KEYS_PER_PASS = kThreads / (D / 8);
-  const bf16* kbase = k + ((size_t)k0 * hkv + g) * D + st_c8;
-  const bf16* vbase = v + ((size_t)k0 * hkv + g) * D + st_c8;
-  const size_t kv_stride = (size_t)hkv * D;
-  // 64 consecutive keys starting at key0.
-  auto gload = [&](u32x4 (&dst)[S::PER_THREAD], const bf16* base, int key0) {
+  // Sequence bases are wave-uniform; each lane adds fixed 32-bit byte offsets
+  // (64 rows of hkv * D bf16 stay far below 4 GiB), so a tile that lies wholly
+  // inside the sequence needs no per-lane address arithmetic. Only the tail
+  // tile clamps rows one by one.
+  const char* kbase = (const char*)(k + ((size_t)k0 * hkv + g) * D);
+  const char* vbase = (const char*)(v + ((size_t)k0 * hkv + g) * D);
+  const size_t row_bytes = (size_t)hkv * D * sizeof(bf16);
+  uint32_t st_off[S::PER_THREAD];
 #pragma unroll
-    for (int i = 0; i < S::PER_THREAD; ++i) {
-      const int kk = min(key0 + st_key + i * KEYS_PER_PASS, lk - 1);
-      dst[i] = *(const u32x4*)(base + (size_t)kk * kv_stride);
+  for (int i = 0; i < S::PER_THREAD; ++i)
+    st_off[i] = (uint32_t)((st_key + i * KEYS_PER_PASS) * row_bytes + st_c8 * sizeof(bf16));
+  // 64 consecutive keys starting at key0.
+  auto gload = [&](u32x4 (&dst)[S::PER_THREAD], const char* base, int key0) {
+    if (key0 + kBN <= lk) {
+      const char* tile = base + (size_t)key0 * row_bytes;
+#pragma unroll
+      for (int i = 0; i < S::PER_THREAD; ++i) dst[i] = *(const u32x4*)(tile + st_off[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < S::PER_THREAD; ++i) {
+        const int kk = min(key0 + st_key + i * KEYS_PER_PASS, lk - 1);
+        dst[i] = *(const u32x4*)(base + (size_t)kk * row_bytes + st_c8 * sizeof(bf16));
+      }
     }
   };
   // V: one 64-key tile per buffer.
@@ -219,74 +233,87 @@ attn_fwd_bf16_kernel(
   for (int qb = 0; qb < NQ; ++qb)
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) acc[qb][i] = f32x16{};
-  // Running reference max (raw score units) and running sum per column. The
-  // reference is only moved when some column's block max exceeds it by more
-  // than 2^8 in probability terms, so most blocks skip the rescale of O.
-  float m_run[NQ], l_run[NQ];
+  // Per column: reference max m_run (raw score units; -inf until the column
+  // has seen a visible key), the same reference pre-scaled to log2 units, and
+  // the running sum of probabilities against it.
+  float m_run[NQ], mref[NQ], l_run[NQ];
 #pragma unroll
   for (int qb = 0; qb < NQ; ++qb) {
     m_run[qb] = neg_inf();
+    mref[qb] = 0.f;
     l_run[qb] = 0.f;
   }
-  const float tau = 8.f / scale_log2;
+  // The reference only has to keep probabilities finite (bf16 P and the fp32
+  // sums share fp32's exponent range), not at or below 1. So the fast path
+  // takes exponentials against the current reference and checks their sum:
+  // only a sum above 2^32 (a score more than 32 log2 units above the
+  // reference) or a column without a reference yet takes the slow path, which
+  // moves the reference to the exact running max, rescales O and the sum, and
+  // recomputes. This drops the per-block max from the common path.
+  constexpr float kSumLimit = 4294967296.f;
 
   // Softmax and PV for sub-block sb of tile j (keys j*64 + sb*32 ...).
   auto softmax_pv = [&](auto masked, f32x16 (&s)[NQ], int j, int sb) {
-    float lm[NQ];
-    bool need_any = false;
-    bool need[NQ];
+    if constexpr (decltype(masked)::value) {
 #pragma unroll
-    for (int qb = 0; qb < NQ; ++qb) {
-      if constexpr (decltype(masked)::value) {
+      for (int qb = 0; qb < NQ; ++qb) {
         const int lim = CAUSAL ? min(lk - 1, tq[qb] + diag) : lk - 1;
         const int kb0 = j * kBN + sb * 32 + half * 4;
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           if (kb0 + (r >> 2) * 8 + (r & 3) > lim) s[qb][r] = neg_inf();
       }
-      float x = neg_inf();
-#pragma unroll
-      for (int r = 0; r < 16; ++r) x = fmaxf(x, s[qb][r]);
-      // The other lane half holds the other keys of the same column.
-      auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-      lm[qb] = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-      need[qb] = lm[qb] > m_run[qb] + tau;
-      need_any |= need[qb];
     }
-    if (__builtin_amdgcn_ballot_w64(need_any)) {
+    float e[NQ][16], ts[NQ];
+    auto exps = [&]() {
 #pragma unroll
       for (int qb = 0; qb < NQ; ++qb) {
-        const float m_new = need[qb] ? lm[qb] : m_run[qb];
-        // Columns that keep their reference scale by exactly 1 (their m_run may
-        // be -inf); a reference moving up from -inf scales the (zero) history by 0.
-        const float alpha = need[qb] ? fast_exp2((m_run[qb] - m_new) * scale_log2) : 1.f;
+        ts[qb] = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          e[qb][r] = fast_exp2(__builtin_fmaf(s[qb][r], scale_log2, -mref[qb]));
+          ts[qb] += e[qb][r];   // fp32 sum of the unrounded probabilities: lse stays fp32-accurate
+        }
+      }
+    };
+    exps();
+    bool slow = false;
+#pragma unroll
+    for (int qb = 0; qb < NQ; ++qb) slow |= !(ts[qb] <= kSumLimit) || m_run[qb] == neg_inf();
+    if (__builtin_amdgcn_ballot_w64(slow)) {
+#pragma unroll
+      for (int qb = 0; qb < NQ; ++qb) {
+        float x = neg_inf();
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x = fmaxf(x, s[qb][r]);
+        // The other lane half holds the other keys of the same column.
+        auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        const float m_new = fmaxf(m_run[qb], fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])));
+        // Unchanged references scale by exactly 1 (m_run may be -inf); one moving
+        // up from -inf scales the (zero) history by 0.
+        const float alpha = m_new == m_run[qb] ? 1.f : fast_exp2((m_run[qb] - m_new) * scale_log2);
         m_run[qb] = m_new;
+        mref[qb] = m_new == neg_inf() ? 0.f : m_new * scale_log2;
         l_run[qb] *= alpha;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[qb][db][r] *= alpha;
       }
+      exps();
     }
-    // Probabilities against the reference; P^T (B operand) for the two 16-key steps.
+    // P^T (B operand) for the two 16-key steps.
     bf16x8 p[NQ][2];
 #pragma unroll
     for (int qb = 0; qb < NQ; ++qb) {
-      const float mref = m_run[qb] == neg_inf() ? 0.f : m_run[qb] * scale_log2;
-      float ts = 0.f;
+      l_run[qb] += ts[qb];
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         bf16x2 pr[4];
 #pragma unroll
-        for (int y = 0; y < 4; ++y) {
-          const float e0 = fast_exp2(__builtin_fmaf(s[qb][hh * 8 + 2 * y], scale_log2, -mref));
-          const float e1 = fast_exp2(__builtin_fmaf(s[qb][hh * 8 + 2 * y + 1], scale_log2, -mref));
-          pr[y] = f32x2_to_bf16x2(e0, e1);
-          ts += e0 + e1;   // fp32 sum of the unrounded probabilities: lse stays fp32-accurate
-        }
+        for (int y = 0; y < 4; ++y) pr[y] = f32x2_to_bf16x2(e[qb][hh * 8 + 2 * y], e[qb][hh * 8 + 2 * y + 1]);
         p[qb][hh] = bf16x8{pr[0][0], pr[0][1], pr[1][0], pr[1][1], pr[2][0], pr[2][1], pr[3][0], pr[3][1]};
       }
-      l_run[qb] += ts;
     }
 
     // O^T += V^T P^T over the sub-block's two 16-key steps; each V^T read feeds NQ MFMAs.
