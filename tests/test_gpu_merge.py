@@ -40,6 +40,25 @@ def test_attn_update_random(sp, hd, go_dtype):
           "fp32" if go_dtype == "fp32" else "bf16")
 
 
+@pytest.mark.parametrize("go_dtype,bsh", [("fp32", 20003), ("bf16", 40001)])
+def test_attn_update_large_partials(go_dtype, bsh):
+    """Partials of 64 MiB and more take the plain-load variant of the kernel."""
+    torch = need_gpu()
+    sp, hd = 8, 128
+    rng = np.random.default_rng(bsh)
+    lse, go = _random_partials(rng, sp, bsh, hd)
+    if go_dtype == "bf16":
+        from varlen_flash_attention_amd.workloads import round_to_bf16
+        go = round_to_bf16(go)
+    assert sp * bsh * hd * (4 if go_dtype == "fp32" else 2) >= 64 << 20
+    print(f"[case] attn_update large sp={sp} hd={hd} go={go_dtype} bsh={bsh}", flush=True)
+    out, lse_out = vfa.attn_update(torch.from_numpy(lse).cuda(), dev_array(go, go_dtype), 1)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.attn_update(lse, go, 1)
+    check(f"attn_update large {go_dtype}", host64(out), host64(lse_out), ref_o, ref_l,
+          "fp32" if go_dtype == "fp32" else "bf16")
+
+
 def test_attn_update_type0_leaves_lse_out():
     torch = need_gpu()
     rng = np.random.default_rng(7)
