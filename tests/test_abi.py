@@ -150,7 +150,7 @@ def test_workspace_size_plan(lib):
     # Decode-shaped calls (G heads x query tokens <= 16, long keys) get a split-KV workspace of
     # n_splits * total_q * Hq * (D + 1) fp32 values; prefill-shaped calls need none.
     ws = lib.varlen_attn_fwd_workspace_size
-    assert ws(64, 64, 1, 32768, 32, 4, 128) == 32 * 64 * 32 * 129 * 4      # 1024-key splits
+    assert ws(64, 64, 1, 32768, 32, 4, 128) == 8 * 64 * 32 * 129 * 4       # 4096-key splits
     assert ws(2, 2, 1, 4096, 32, 4, 128) == 16 * 2 * 32 * 129 * 4          # 256-key splits for a small batch
     assert ws(16, 46000, 8192, 8192, 32, 8, 128) == 0                       # prefill
     assert ws(64, 64, 1, 300, 32, 4, 128) == 0                              # short keys: no split

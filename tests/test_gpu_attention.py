@@ -153,6 +153,8 @@ def test_bf16_in_fp32_out():
     (16, 2, 2, 128, True),    # 2 query tokens x 8 heads fill the 16 columns; the causal mask bites
     (8, 8, 1, 128, True),     # G = 1
     (12, 4, 5, 128, True),    # G = 3 with 5 tokens: 15 of 16 columns
+    (8, 1, 1, 128, True),     # one kv head: one head per workgroup, four waves split its keys
+    (24, 3, 1, 64, False),    # odd kv head count: one head per workgroup
 ])
 def test_decode_variants(hq, hkv, lq, d, causal):
     lk = [1500, 600, 4099, 0, 513, 2048]
