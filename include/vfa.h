@@ -14,6 +14,18 @@
  *     returns its status code and launches nothing. After a launch, a HIP
  *     launch error is reported as VFA_ERR_LAUNCH.
  *   - Return values are vfa_status codes (0 = success).
+ *   - Debug check: with the environment variable VFA_DEBUG set to anything but
+ *     "" or "0" (read on every call), varlen_attn_fwd and
+ *     varlen_last_token_gather first check the cu_seqlens contract on the
+ *     device:
+ *       - cu[0] == 0;
+ *       - entries non-decreasing;
+ *       - cu[batch] equals the total (attention only);
+ *       - no length above the max_seqlen bound.
+ *     A violation returns VFA_ERR_SHAPE and launches nothing. The check
+ *     synchronises the stream, copies one word to the host and clears a
+ *     library word in device memory with hipMemsetAsync. Debug calls must not
+ *     be captured into a graph or run concurrently on one device.
  *
  * The argument conventions follow the problem as the source pages state it:
  *   [P1] "From GPU to NPU: Qwen3-Embedding model adaptation and performance
@@ -87,7 +99,8 @@ size_t varlen_attn_fwd_workspace_size(int32_t batch, int32_t total_q,
  * k, v    [total_k, num_heads_kv, head_dim]   in_dtype
  * cu_seqlens_q, cu_seqlens_k: device int32 [batch + 1], cu[0] = 0,
  *         non-decreasing, cu_q[batch] = total_q, cu_k[batch] = total_k.
- *         Not read on the host and not checked (caller contract).
+ *         Not read on the host and not checked (caller contract), except
+ *         on the device under VFA_DEBUG (see above).
  * max_seqlen_q / max_seqlen_k: host upper bounds of the per-sequence
  *         lengths; they size the launch so that no device-to-host copy of
  *         cu_seqlens is needed ([P1] core optimisation 1 keeps cu_seqlens

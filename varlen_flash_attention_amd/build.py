@@ -24,7 +24,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libvfa.so")
 
-SOURCES = ["api.cpp", "attn_fwd_bf16.hip", "attn_decode.hip", "attn_fwd_f32.hip", "attn_update.hip"]
+SOURCES = ["api.cpp", "attn_fwd_bf16.hip", "attn_decode.hip", "attn_fwd_f32.hip", "attn_update.hip",
+           "debug_check.hip"]
 ARCH = "gfx950"
 
 

@@ -12,6 +12,8 @@
 // and core optimisation 5: head counts, TND layout, per-sequence lengths,
 // scale, causal flag).
 #include <cmath>
+#include <cstdlib>
+#include <cstring>
 #include <cstdint>
 
 #include "../../include/vfa.h"
@@ -50,6 +52,13 @@ DecodePlan plan_decode(int batch, int total_q, int max_seqlen_q, int max_seqlen_
 namespace {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// VFA_DEBUG set to anything but "" or "0": check cu_seqlens on the device
+// before launching (read on every call, so a process can switch it).
+bool debug_checks() {
+  const char* e = std::getenv("VFA_DEBUG");
+  return e && *e && std::strcmp(e, "0") != 0;
+}
 
 }  // namespace
 
@@ -101,6 +110,13 @@ VFA_API int32_t varlen_attn_fwd(const void* q, const void* k, const void* v, int
   if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return VFA_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return VFA_ERR_UNSUPPORTED;
 
+  if (debug_checks()) {
+    const int r = vfa::check_cu_seqlens(cu_seqlens_q, total_q, max_seqlen_q, cu_seqlens_k, total_k, max_seqlen_k,
+                                        batch, stream);
+    if (r < 0) return VFA_ERR_LAUNCH;
+    if (r > 0) return VFA_ERR_SHAPE;
+  }
+
   vfa::AttnArgs a{};
   a.q = q; a.k = k; a.v = v;
   a.cu_q = cu_seqlens_q; a.cu_k = cu_seqlens_k;
@@ -144,6 +160,11 @@ VFA_API int32_t varlen_last_token_gather(const void* x, int32_t dtype, const int
   if (batch == 0 || row_elems == 0) return VFA_OK;
   if (!x || !cu_seqlens || !out) return VFA_ERR_NULL;
   if (dtype != VFA_F32 && dtype != VFA_BF16) return VFA_ERR_UNSUPPORTED;
+  if (debug_checks()) {
+    const int r = vfa::check_cu_seqlens(cu_seqlens, -1, 0x7fffffff, nullptr, 0, 0, batch, stream);
+    if (r < 0) return VFA_ERR_LAUNCH;
+    if (r > 0) return VFA_ERR_SHAPE;
+  }
   return vfa::launch_last_token_gather(x, dtype == VFA_F32 ? 4 : 2, cu_seqlens, batch, row_elems, out, stream) == 0
              ? VFA_OK
              : VFA_ERR_LAUNCH;

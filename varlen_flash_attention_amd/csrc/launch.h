@@ -44,4 +44,11 @@ int launch_attn_update(const float* lse, const void* go, int go_dtype, int sp, i
 int launch_last_token_gather(const void* x, int esize, const int32_t* cu, int batch, int64_t row_elems,
                              void* out, void* stream);
 
+// Caller-contract check of one or two cu_seqlens arrays of batch + 1 entries
+// (cu_b may be NULL; a negative total skips the end check). Synchronises the
+// stream. Returns 0 if the contract holds, 1 if it is violated, -1 on a HIP
+// error.
+int check_cu_seqlens(const int32_t* cu_a, int total_a, int max_a, const int32_t* cu_b, int total_b, int max_b,
+                     int batch, void* stream);
+
 }  // namespace vfa
