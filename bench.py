@@ -108,6 +108,8 @@ def attn_case(vfa, torch, w, reps=20, warmup=3, gather=False):
         "useful_tflops": round(flops / t / 1e9, 2), "frac_bf16_peak": round(flops / t / 1e9 / PEAK_BF16_TFLOPS, 4),
         "compulsory_gb_per_s": round(byt / t / 1e6, 1), "frac_hbm_peak": round(byt / t / 1e6 / PEAK_HBM_GBPS, 4),
         "useful_gflop": round(flops / 1e9, 3), "compulsory_mb": round(byt / 1e6, 2),
+        # time at the binding roofline, min(MFMA peak, HBM peak x intensity), over the measured time
+        "frac_attainable_roofline": round(max(flops / (PEAK_BF16_TFLOPS * 1e9), byt / (PEAK_HBM_GBPS * 1e6)) / t, 4),
         "total_q": w.total_q, "total_k": w.total_k, "batch": w.batch, "seed": w.seed,
     }
     del d, out, lse, ws, last
@@ -125,10 +127,13 @@ def merge_case(vfa, torch, reps=100, warmup=5):
     out = torch.empty((bsh, hd), dtype=torch.float32, device="cuda")
     lse_out = torch.empty((bsh,), dtype=torch.float32, device="cuda")
     algo_bytes = sp * bsh * (hd + 1) * 4 + bsh * (hd + 1) * 4            # 9,510,912 B
-    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    scratch = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
 
     def flush():
-        scratch.fill_(1)        # 1 GiB write evicts L2 and the infinity cache
+        # Read 1 GiB of other data: evicts the inputs from L2 and the last-level
+        # cache and leaves it clean. (A 1 GiB write would leave it full of dirty
+        # lines, so the timed reads would first pay for their write-back.)
+        scratch.sum()
 
     def call():
         vfa.attn_update(lse, go, 1, out=out, lse_out=lse_out)
@@ -147,23 +152,29 @@ def merge_case(vfa, torch, reps=100, warmup=5):
                      "frac_hbm_peak": round(algo_bytes / t / 1e6 / PEAK_HBM_GBPS, 4)}
     res["algorithmic_bytes"] = algo_bytes
     res["shape"] = {"sp": sp, "bsh": bsh, "hd": hd, "dtype": "fp32"}
-    del scratch, csrc, cdst, go, out, lse, lse_out
+    del csrc, cdst, go, out, lse, lse_out
     torch.cuda.empty_cache()
 
-    # The same kernel on 32x the rows (302 MB, larger than the last-level
-    # cache): what it sustains once launch and first-byte latency amortise.
-    big = 32 * bsh
-    lse = torch.randn((sp, big), dtype=torch.float32, device="cuda")
-    go = torch.randn((sp, big, hd), dtype=torch.float32, device="cuda")
-    out = torch.empty((big, hd), dtype=torch.float32, device="cuda")
-    lse_out = torch.empty((big,), dtype=torch.float32, device="cuda")
-    big_bytes = sp * big * (hd + 1) * 4 + big * (hd + 1) * 4
-    ms = time_calls(lambda: vfa.attn_update(lse, go, 1, out=out, lse_out=lse_out), 20, 3, torch)
-    t = median(ms)
-    res["rows_x32"] = {"us_median": round(t * 1e3, 3), "gb_per_s": round(big_bytes / t / 1e6, 1),
-                       "frac_hbm_peak": round(big_bytes / t / 1e6 / PEAK_HBM_GBPS, 4),
-                       "algorithmic_bytes": big_bytes, "bsh": big}
-    del lse, go, out, lse_out
+    # The same kernel on 4x .. 64x the rows, cold: the bandwidth asymptote
+    # once launch and first-byte latency amortise (64x is 608 MB, beyond the
+    # last-level cache).
+    sweep = {}
+    for mult in (4, 16, 64):
+        big = mult * bsh
+        lse = torch.randn((sp, big), dtype=torch.float32, device="cuda")
+        go = torch.randn((sp, big, hd), dtype=torch.float32, device="cuda")
+        out = torch.empty((big, hd), dtype=torch.float32, device="cuda")
+        lse_out = torch.empty((big,), dtype=torch.float32, device="cuda")
+        big_bytes = sp * big * (hd + 1) * 4 + big * (hd + 1) * 4
+        ms = time_calls(lambda: vfa.attn_update(lse, go, 1, out=out, lse_out=lse_out), 20, 3, torch, flush=flush)
+        t = median(ms)
+        sweep[f"rows_x{mult}"] = {"bsh": big, "algorithmic_bytes": big_bytes, "us_median": round(t * 1e3, 3),
+                                  "gb_per_s": round(big_bytes / t / 1e6, 1),
+                                  "frac_hbm_peak": round(big_bytes / t / 1e6 / PEAK_HBM_GBPS, 4)}
+        del lse, go, out, lse_out
+        torch.cuda.empty_cache()
+    res["size_sweep_cold"] = sweep
+    del scratch
     torch.cuda.empty_cache()
     return res
 

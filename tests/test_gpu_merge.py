@@ -40,22 +40,25 @@ def test_attn_update_random(sp, hd, go_dtype):
           "fp32" if go_dtype == "fp32" else "bf16")
 
 
-@pytest.mark.parametrize("go_dtype,bsh", [("fp32", 20003), ("bf16", 40001)])
-def test_attn_update_large_partials(go_dtype, bsh):
-    """Partials of 64 MiB and more take the plain-load variant of the kernel."""
+@pytest.mark.parametrize("go_dtype,sp,bsh,hd", [
+    ("fp32", 8, 20003, 128),    # 2501 workgroups: one row per thread
+    ("fp32", 8, 40003, 128),    # 5001 workgroups: two rows per thread, ragged last pair
+    ("bf16", 2, 65537, 128),    # two rows per thread, one row past the last full pair
+    ("bf16", 3, 140003, 64),    # hd = 64, two rows per thread
+])
+def test_attn_update_large(go_dtype, sp, bsh, hd):
+    """Large merges (at least 4096 workgroups of rows) take the two-rows-per-thread variant."""
     torch = need_gpu()
-    sp, hd = 8, 128
-    rng = np.random.default_rng(bsh)
+    rng = np.random.default_rng(bsh + sp)
     lse, go = _random_partials(rng, sp, bsh, hd)
     if go_dtype == "bf16":
         from varlen_flash_attention_amd.workloads import round_to_bf16
         go = round_to_bf16(go)
-    assert sp * bsh * hd * (4 if go_dtype == "fp32" else 2) >= 64 << 20
     print(f"[case] attn_update large sp={sp} hd={hd} go={go_dtype} bsh={bsh}", flush=True)
     out, lse_out = vfa.attn_update(torch.from_numpy(lse).cuda(), dev_array(go, go_dtype), 1)
     torch.cuda.synchronize()
     ref_o, ref_l = oracle.attn_update(lse, go, 1)
-    check(f"attn_update large {go_dtype}", host64(out), host64(lse_out), ref_o, ref_l,
+    check(f"attn_update large {go_dtype} sp={sp} bsh={bsh}", host64(out), host64(lse_out), ref_o, ref_l,
           "fp32" if go_dtype == "fp32" else "bf16")
 
 

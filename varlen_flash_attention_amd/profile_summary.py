@@ -17,6 +17,10 @@ TRACE_CMD = ("cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d
 PMC_CMD = ("cd /tmp && rocprofv3 --pmc {c} --output-format csv -d <dir>/{c} -o bench -- "
            "python3 <repo>/bench.py --no-cpu --steps 3 --warmup 1 --copy-calibration")
 HEAD = "attn_fwd_bf16_kernelILi8ELi1ELi128ELb1EDF16b"   # 8 waves x 32 columns, D=128, causal, bf16 out
+MERGE = "attn_update_kernel<float, 128, 8, true>"       # the merge config shape (streaming loads)
+MERGE_BYTES = 9510912                                   # sp*bsh*(hd+1)*4 + bsh*(hd+1)*4 at sp=8, bsh=2048, hd=128
+MERGE_GRID = 2048 * 32                                  # threads: 32 lanes per row at hd=128, fp32
+FLUSH = ("reduce_kernel", "FillFunctor")               # the 1 GiB cache flush before each cold call
 COPY = "__amd_rocclr_copyBuffer"
 COPY_BYTES = 1 << 28
 
@@ -58,6 +62,30 @@ def main(src, dst):
               "timed launch durations (us): " + ", ".join(f"{x:.0f}" for x in timed)]
     os.makedirs(dst, exist_ok=True)
     open(os.path.join(dst, "attn_fwd_bf16_long_prefill.kernel_stats.txt"), "w").write("\n".join(lines) + "\n")
+
+    # Merge at the config shape: kernel durations, cold (right after the flush) and warm.
+    cold, warm = [], []
+    for prev, r in zip(trace, trace[1:]):
+        if MERGE in r["Kernel_Name"] and int(r.get("Grid_Size_X", MERGE_GRID)) == MERGE_GRID:
+            us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            (cold if any(f in prev["Kernel_Name"] for f in FLUSH) else warm).append(us)
+    if cold:
+        def q(xs, f):
+            ys = sorted(xs)
+            return ys[min(len(ys) - 1, int(f * len(ys)))]
+        ml = ["# rocprofv3 kernel durations of attn_update at the merge shape (sp=8, bsh=2048, hd=128, fp32)", "",
+              "command: the kernel trace above (bench.py's merge case: cold calls follow a 1 GiB read that "
+              "evicts L2 and the last-level cache; warm calls are queued back to back)",
+              "summarised by: python -m varlen_flash_attention_amd.profile_summary <dir> profiles", "",
+              f"algorithmic bytes per call: {MERGE_BYTES}", ""]
+        for name, xs in (("cold", cold), ("warm", warm)):
+            if not xs:
+                continue
+            med = q(xs, 0.5)
+            ml.append(f"{name}: {len(xs)} calls, kernel median {med:.2f} us (p10 {q(xs, 0.1):.2f}, "
+                      f"p90 {q(xs, 0.9):.2f}) -> {MERGE_BYTES / med / 1e3:.0f} GB/s, "
+                      f"{MERGE_BYTES / med / 1e3 / 8000:.1%} of 8 TB/s")
+        open(os.path.join(dst, "attn_update_merge.kernel_durations.txt"), "w").write("\n".join(ml) + "\n")
 
     def counter(c):
         per = collections.defaultdict(list)
