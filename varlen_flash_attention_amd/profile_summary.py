@@ -17,7 +17,7 @@ TRACE_CMD = ("cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d
 PMC_CMD = ("cd /tmp && rocprofv3 --pmc {c} --output-format csv -d <dir>/{c} -o bench -- "
            "python3 <repo>/bench.py --no-cpu --steps 3 --warmup 1 --copy-calibration")
 HEAD = "attn_fwd_bf16_kernelILi8ELi1ELi128ELb1EDF16b"   # 8 waves x 32 columns, D=128, causal, bf16 out
-MERGE = "attn_update_kernel<float, 128, 8, true>"       # the merge config shape (streaming loads)
+MERGE = "attn_update_kernel<float, 128, 8, 1>"          # the merge config shape (one row per thread)
 MERGE_BYTES = 9510912                                   # sp*bsh*(hd+1)*4 + bsh*(hd+1)*4 at sp=8, bsh=2048, hd=128
 MERGE_GRID = 2048 * 32                                  # threads: 32 lanes per row at hd=128, fp32
 FLUSH = ("reduce_kernel", "FillFunctor")               # the 1 GiB cache flush before each cold call
@@ -111,8 +111,8 @@ def main(src, dst):
         tl.append(f"{len(fetch[name]):6d} {f_b/1e6:10.2f} {w_b/1e6:10.2f}  {short(name)}")
         if HEAD in name:
             rec = (sum(fetch[name]) / len(fetch[name]), sum(write[name]) / len(write[name]), f_b, w_b)
-    tl += ["", "attn_update_kernel<float, 128, 8, true> runs the 2048-row merge shape (cold and warm calls "
-           "averaged); <..., false> the 65536-row shape."]
+    tl += ["", "attn_update_kernel<float, 128, 8, 1> runs the 2048-row merge shape (cold and warm calls "
+           "averaged, plus the 4x sweep point); <..., 2> the 16x and 64x sweep points (two rows per thread)."]
     open(os.path.join(dst, "bench_kernels.hbm_traffic.txt"), "w").write("\n".join(tl) + "\n")
 
     sha = hashlib.sha256(open(os.path.join(repo, "varlen_flash_attention_amd", "csrc", "attn_fwd_bf16.hip"),
