@@ -339,12 +339,14 @@ attn_fwd_bf16_kernel(
   // iteration separates every LDS write from the reads of the same slot.
   const int n_sub = 2 * n_tiles;
   if (n_tiles > 0) {
+    // All three first loads in flight together (one memory round trip).
+    u32x4 kst2[S::PER_THREAD];
     gload(kst, kbase, 0);
     gload(vst, vbase, 0);
+    gload(kst2, kbase, 64);
     sstore_k(kst, 0);
     sstore_v(vst, vbufs);
-    gload(kst, kbase, 64);
-    sstore_k(kst, 2);
+    sstore_k(kst2, 2);
   }
   __syncthreads();
   if (n_sub > 3) gload(kst, kbase, 3 * 32);
