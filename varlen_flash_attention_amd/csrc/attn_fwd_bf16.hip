@@ -33,6 +33,10 @@
 #include "common.h"
 #include "launch.h"
 
+// Kernel-body lambdas are forced inline: one left out of line takes the
+// register arrays it touches by reference, which moves them to scratch.
+#define VFA_INLINE __attribute__((always_inline))
+
 namespace vfa {
 namespace {
 
@@ -374,29 +378,44 @@ attn_fwd_bf16_kernel(
   for (; j < n_tiles; ++j) tile_step(std::integral_constant<bool, true>{}, j);
 
   // Epilogue: combine the two lane halves' partial sums, normalise, store.
+  // A lane holds, per 32-dim block and group g4, the 4 dims g4*8 + half*4 ..;
+  // for bf16 output the two halves trade one group of each pair (lane i and
+  // i + 32 own the same query), so each lane stores 8 contiguous dims (16 B)
+  // instead of 4.
 #pragma unroll
   for (int qb = 0; qb < NQ; ++qb) {
     const float l_tot = l_run[qb] + xor_shuffle(l_run[qb], 32);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    if (!qvalid[qb]) continue;
     const size_t row = (size_t)(q0 + tq[qb]) * hq + head[qb];
     OutT* orow = out + row * D;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+    for (int db = 0; db < D / 32; ++db) {
+      const f32x16& a = acc[qb][db];
+      if constexpr (sizeof(OutT) == 2) {
+        auto pk = [&](int r) VFA_INLINE {
+          return __builtin_bit_cast(uint32_t, f32x2_to_bf16x2(a[r] * inv, a[r + 1] * inv));
+        };
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d0 = db * 32 + g4 * 8 + half * 4;
-        const f32x16& a = acc[qb][db];
-        if constexpr (sizeof(OutT) == 2) {
-          bf16x2 x0 = f32x2_to_bf16x2(a[g4 * 4 + 0] * inv, a[g4 * 4 + 1] * inv);
-          bf16x2 x1 = f32x2_to_bf16x2(a[g4 * 4 + 2] * inv, a[g4 * 4 + 3] * inv);
-          *(bf16x4*)(orow + d0) = bf16x4{x0[0], x0[1], x1[0], x1[1]};
-        } else {
-          *(f32x4*)(orow + d0) =
-              f32x4{a[g4 * 4 + 0] * inv, a[g4 * 4 + 1] * inv, a[g4 * 4 + 2] * inv, a[g4 * 4 + 3] * inv};
+        for (int gp = 0; gp < 2; ++gp) {
+          const int ga = 2 * gp, gb = 2 * gp + 1;   // half 0 stores group ga, half 1 group gb
+          const uint32_t a0 = pk(ga * 4), a1 = pk(ga * 4 + 2), b0 = pk(gb * 4), b1 = pk(gb * 4 + 2);
+          // Lanes 0-31 receive the upper half's group ga, lanes 32-63 the lower half's group gb.
+          const auto s0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
+          const auto s1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
+          const u32x4 val = half == 0 ? u32x4{a0, a1, s0[1], s1[1]} : u32x4{s0[0], s1[0], b0, b1};
+          u32x4* dst = (u32x4*)(orow + db * 32 + (half == 0 ? ga : gb) * 8);
+          if (qvalid[qb]) *dst = val;
+        }
+      } else {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const f32x4 val{a[g4 * 4 + 0] * inv, a[g4 * 4 + 1] * inv, a[g4 * 4 + 2] * inv, a[g4 * 4 + 3] * inv};
+          f32x4* dst = (f32x4*)(orow + db * 32 + g4 * 8 + half * 4);
+          if (qvalid[qb]) *dst = val;
         }
       }
-    if (half == 0)
+    }
+    if (qvalid[qb] && half == 0)
       lse[row] = l_tot > 0.f ? m_run[qb] * scale + fast_log2(l_tot) * kLn2 : neg_inf();
   }
 }
