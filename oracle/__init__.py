@@ -14,6 +14,10 @@ Parity status per function (what pins it; see tests/test_oracle_*.py):
       unchunked attention, sp = 1 identity, chunk permutation, -inf chunks.
   chunked_partials -- pinned through the chunked + merged == unchunked check.
   last_token_gather -- pinned: golden indices for the tiny workload.
+  paged_gather / paged_attention_rows -- pinned: a hand-worked paged fixture
+      (Q = 0, so each row is the mean of the value rows it gathers) and
+      scatter-into-shuffled-pages equals the contiguous oracle, with NaN in
+      every slot the block table does not name.
 """
 from .attention import (  # noqa: F401
     varlen_attention,
@@ -21,4 +25,6 @@ from .attention import (  # noqa: F401
     attn_update,
     last_token_gather,
     chunked_partials,
+    paged_gather,
+    paged_attention_rows,
 )

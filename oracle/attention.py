@@ -24,7 +24,8 @@ Sources (page title, section):
        description (the four-line lse_max / lse / lse_m / O formula) and the
        InferShape / op-plugin sections (lse [sp, bsh], go [sp, bsh, hd] ->
        out [bsh, hd], lse_out [bsh]; out takes go's dtype; lse_out only when
-       update_type == 1).
+       update_type == 1). Its background section names PagedAttention as the
+       operator whose per-chunk partials the merge combines.
 
 Readings where the pages are silent (each also listed in the design notes):
   * cu_seqlens: int32, length B+1, cu[0] = 0, non-decreasing ([P1] core
@@ -41,6 +42,12 @@ Readings where the pages are silent (each also listed in the design notes):
   * Chunk c of sp covers keys [floor(c*Lk/sp), floor((c+1)*Lk/sp)); inside a
     chunk the causal mask uses absolute key positions.
   * Merge row order "bsh" is the [T, Hq] flattening r = token * Hq + head.
+  * Paged K/V ([P4] names PagedAttention but gives no cache layout): a cache
+    [num_pages, page_size, Hkv, D] per tensor, an int block table
+    [B, max_pages] and the key count of each sequence; key j of sequence b is
+    slot j % page_size of page block_table[b, j // page_size]. Queries stay
+    in TND with cu_seqlens_q, and the mask is the one above with
+    Lk = the sequence's key count.
 """
 from __future__ import annotations
 
@@ -52,6 +59,8 @@ __all__ = [
     "attn_update",
     "last_token_gather",
     "chunked_partials",
+    "paged_gather",
+    "paged_attention_rows",
 ]
 
 
@@ -228,3 +237,40 @@ def chunked_partials(q, k, v, cu_seqlens_q, cu_seqlens_k, num_heads_kv: int, sca
         lse_all[c] = lse_c.reshape(-1)
         go_all[c] = o_c.reshape(n * hq, -1)
     return lse_all, go_all
+
+
+def paged_gather(cache, block_table, seqused_k):
+    """The key (or value) rows of every sequence, read through its block table.
+
+    cache [num_pages, page_size, Hkv, D]; block_table [B, max_pages] ints;
+    seqused_k [B] ints (keys of each sequence). Key j of sequence b is
+    cache[block_table[b, j // page_size], j % page_size] (the paged-cache
+    reading listed in the module docstring). Returns the rows packed in TND
+    order, [sum_b seqused_k[b], Hkv, D], and their cu_seqlens [B + 1]. Pages
+    and slots that no key of a sequence names are never read.
+    """
+    cache = np.asarray(cache)
+    table = np.asarray(block_table, dtype=np.int64)
+    used = np.asarray(seqused_k, dtype=np.int64)
+    page_size = cache.shape[1]
+    parts = []
+    for b in range(len(used)):
+        j = np.arange(int(used[b]), dtype=np.int64)
+        parts.append(cache[table[b, j // page_size], j % page_size])
+    packed = (np.concatenate(parts, axis=0) if parts else np.zeros((0,) + cache.shape[2:], cache.dtype))
+    cu = np.concatenate([[0], np.cumsum(used)]).astype(np.int64)
+    return packed, cu
+
+
+def paged_attention_rows(q, k_cache, v_cache, block_table, seqused_k, cu_seqlens_q, num_heads_kv: int,
+                         scale: float, causal: bool, tokens=None):
+    """Varlen attention whose keys and values sit in a paged cache.
+
+    Same definition as varlen_attention_rows (TND queries, GQA h -> h // G,
+    bottom-right causal mask, natural-log lse, -inf / 0 for rows without a
+    visible key), with sequence b's keys and values gathered by paged_gather.
+    Returns O [len(tokens), Hq, D] and lse [len(tokens), Hq] in fp64.
+    """
+    k, cu_k = paged_gather(k_cache, block_table, seqused_k)
+    v, _ = paged_gather(v_cache, block_table, seqused_k)
+    return varlen_attention_rows(q, k, v, cu_seqlens_q, cu_k, num_heads_kv, scale, causal, tokens=tokens)

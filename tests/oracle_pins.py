@@ -328,6 +328,73 @@ def check_rows_subset(orc, seed=13):
     _same(ls_, lse[tok], 1e-14)
 
 
+def _num(x):
+    """Golden numbers: plain floats, "a/b" fractions or "lnN"."""
+    if isinstance(x, str):
+        if x.startswith("ln"):
+            return math.log(float(x[2:]))
+        sign = -1.0 if x.startswith("-") else 1.0
+        a, b = x.lstrip("-").split("/")
+        return sign * float(a) / float(b)
+    return float(x)
+
+
+def check_golden_paged(orc):
+    g = _load("paged_handworked.json")
+    ps, npg = g["page_size"], g["num_pages"]
+    v_cache = np.full((npg, ps, 1, 2), np.nan)
+    k_cache = np.full((npg, ps, 1, 2), np.nan)
+    table = np.asarray(g["block_table"])
+    for b, used in enumerate(g["seqused_k"]):          # fill only the slots a key names
+        for j in range(used):
+            p, s = table[b][j // ps], j % ps
+            v_cache[p, s, 0] = [10 * p + s, -(10 * p + s)]
+            k_cache[p, s, 0] = 0.0
+    cu_q = np.asarray(g["cu_seqlens_q"])
+    q = np.zeros((int(cu_q[-1]), 1, 2))
+    out, lse = orc.paged_attention_rows(q, k_cache, v_cache, table, g["seqused_k"], cu_q, 1, 1.0, g["causal"])
+    want_o = np.array([[_num(e) for e in row] for row in g["out"]])
+    want_l = np.array([_num(e) for e in g["lse"]])
+    assert np.allclose(out[:, 0, :], want_o, rtol=1e-14, atol=1e-12), (out[:, 0, :], want_o)
+    assert np.allclose(lse[:, 0], want_l, rtol=1e-14, atol=1e-14), (lse[:, 0], want_l)
+
+
+def check_paged_scatter(orc, seed=17):
+    """Contiguous K/V scattered into shuffled pages, read back through the table, gives the
+    contiguous oracle's result exactly; every slot no key names holds NaN."""
+    rng = np.random.default_rng(seed)
+    for ps in (1, 2, 3, 4, 16):
+        for causal in (True, False):
+            batch = int(rng.integers(1, 5))
+            lk = rng.integers(0, 40, batch)
+            lq = np.minimum(rng.integers(1, 4, batch), np.maximum(lk, 1))
+            hq, hkv, d = 4, 2, 8
+            q = rng.standard_normal((int(lq.sum()), hq, d))
+            k = rng.standard_normal((int(lk.sum()), hkv, d))
+            v = rng.standard_normal((int(lk.sum()), hkv, d))
+            cu_q, cu_k = _cu(lq), _cu(lk)
+            need = [-(-int(n) // ps) for n in lk]
+            max_pages = max(need) + 1
+            num_pages = sum(need) + 5                      # spare pages stay NaN
+            perm = rng.permutation(num_pages)
+            k_cache = np.full((num_pages, ps, hkv, d), np.nan)
+            v_cache = np.full((num_pages, ps, hkv, d), np.nan)
+            table = np.full((batch, max_pages), -1, dtype=np.int64)
+            nxt = 0
+            for b in range(batch):
+                for p in range(need[b]):                   # logical page p of b -> a shuffled physical page
+                    table[b, p] = perm[nxt]
+                    nxt += 1
+                for t in range(int(lk[b])):                # write each key row to its page and slot
+                    phys, slot = table[b, t // ps], t % ps
+                    k_cache[phys, slot] = k[cu_k[b] + t]
+                    v_cache[phys, slot] = v[cu_k[b] + t]
+            o_p, l_p = orc.paged_attention_rows(q, k_cache, v_cache, table, lk, cu_q, hkv, 0.3, causal)
+            o_c, l_c = orc.varlen_attention(q, k, v, cu_q, cu_k, hkv, 0.3, causal)
+            assert np.array_equal(o_p, o_c) and np.array_equal(l_p, l_c), (ps, causal)
+            assert np.all(np.isfinite(o_p))
+
+
 ALL_CHECKS = [
     check_golden_attention,
     check_golden_merge,
@@ -338,4 +405,6 @@ ALL_CHECKS = [
     check_merge_invariants,
     check_attention_invariants,
     check_rows_subset,
+    check_golden_paged,
+    check_paged_scatter,
 ]

@@ -28,6 +28,14 @@ MUTANTS = {
                          "lse_m = np.where(live, safe_max + np.where(live, ssum, 1.0), -np.inf)"),
     "chunk_drops_key": ("return (c * lk) // sp, ((c + 1) * lk) // sp", "return (c * lk) // sp, max((c * lk) // sp, ((c + 1) * lk) // sp - 1)"),
     "gather_first_token": ("idx = cu[1:] - 1", "idx = cu[:-1]"),
+    "paged_page_slot_swapped": ("cache[table[b, j // page_size], j % page_size]",
+                                "cache[table[b, j % page_size], j // page_size]"),
+    "paged_next_page": ("cache[table[b, j // page_size], j % page_size]",
+                        "cache[table[b, (j + 1) // page_size], j % page_size]"),
+    "paged_table_row_of_b0": ("cache[table[b, j // page_size], j % page_size]",
+                              "cache[table[0, j // page_size], j % page_size]"),
+    "paged_drops_last_key": ("j = np.arange(int(used[b]), dtype=np.int64)",
+                             "j = np.arange(max(int(used[b]) - 1, 0), dtype=np.int64)"),
 }
 
 
