@@ -11,8 +11,9 @@ head, key), masked pairs excluded. One JSON line is printed.
 
 Extra fields (not the headline): the embedding-style prefill with the
 last-token gather, the same long prefill without masking, decode against
-long KV sets, and the attn_update merge of the chunked-context config
-(sp=8, bsh=2048, hd=128, fp32) timed with caches flushed before every rep.
+long KV sets (contiguous, and paged with 16- and 128-key pages), and the
+attn_update merge of the chunked-context config (sp=8, bsh=2048, hd=128,
+fp32) timed with caches flushed before every rep.
 
 "roofline" is the attention kernel's achieved useful FLOP rate (per-launch
 HIP-event durations on the launch stream) against the bf16 dense MFMA peak;
@@ -99,10 +100,18 @@ def attn_case(vfa, torch, w, reps=20, warmup=3, gather=False):
             vfa.varlen_last_token_gather(out, d["cu_q"], out=last)
 
     ms = time_calls(call, reps, warmup, torch)
+    res = attn_stats(w, ms)
+    del d, out, lse, ws, last
+    torch.cuda.empty_cache()
+    return res
+
+
+def attn_stats(w, ms, extra_bytes=0):
+    """Median / p10 / p90 of per-call times (ms), useful TFLOP/s and compulsory-byte GB/s."""
     t = median(ms)
     flops = w.useful_flops()
-    byt = w.compulsory_bytes()
-    res = {
+    byt = w.compulsory_bytes() + extra_bytes
+    return {
         "ms_median": round(t, 4), "ms_p10": round(sorted(ms)[len(ms) // 10], 4),
         "ms_p90": round(sorted(ms)[(9 * len(ms)) // 10], 4),
         "useful_tflops": round(flops / t / 1e9, 2), "frac_bf16_peak": round(flops / t / 1e9 / PEAK_BF16_TFLOPS, 4),
@@ -112,7 +121,38 @@ def attn_case(vfa, torch, w, reps=20, warmup=3, gather=False):
         "frac_attainable_roofline": round(max(flops / (PEAK_BF16_TFLOPS * 1e9), byt / (PEAK_HBM_GBPS * 1e6)) / t, 4),
         "total_q": w.total_q, "total_k": w.total_k, "batch": w.batch, "seed": w.seed,
     }
-    del d, out, lse, ws, last
+
+
+def paged_case(vfa, torch, w, page_size, reps=20, warmup=3):
+    """paged_attn_decode on workload w with its K/V in a paged cache (shuffled pages of page_size keys)."""
+    import numpy as np
+    from varlen_flash_attention_amd.workloads import bf16_bits, make_paged
+
+    pc = make_paged(w, page_size, seed=7)
+
+    def dev(x):
+        return torch.from_numpy(bf16_bits(x).view(np.int16)).cuda().view(torch.bfloat16)
+
+    q, kc, vc = dev(w.q), dev(pc.k_cache), dev(pc.v_cache)
+    table = torch.from_numpy(pc.block_table).cuda()
+    used = torch.from_numpy(pc.seqused_k).cuda()
+    cu_q = torch.from_numpy(w.cu_seqlens_q).cuda()
+    del pc
+    out = torch.empty((w.total_q, w.num_heads_q, w.head_dim), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w.total_q, w.num_heads_q), dtype=torch.float32, device="cuda")
+    ws_bytes = vfa.paged_attn_decode_workspace_size(w.batch, w.total_q, w.max_seqlen_q, w.max_seqlen_k,
+                                                    w.num_heads_q, w.num_heads_kv, w.head_dim)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+
+    def call():
+        vfa.paged_attn_decode(q, kc, vc, table, cu_q, used, w.max_seqlen_q, w.max_seqlen_k, softmax_scale=w.scale,
+                              causal=w.causal, out=out, lse=lse, workspace=ws)
+
+    ms = time_calls(call, reps, warmup, torch)
+    # block-table entries the call reads, on top of Q, K, V, O and lse
+    res = attn_stats(w, ms, extra_bytes=int(sum(-(-int(n) // page_size) for n in w.lengths_k)) * 4)
+    res["page_size"] = page_size
+    del q, kc, vc, table, used, cu_q, out, lse, ws
     torch.cuda.empty_cache()
     return res
 
@@ -300,7 +340,12 @@ def main() -> int:
         log("[bench] extra: long_prefill non-causal")
         extra["long_prefill_full"] = attn_case(vfa, torch, make_workload("long_prefill_full"))
         log("[bench] extra: decode")
-        extra["decode"] = attn_case(vfa, torch, make_workload("decode"))
+        wd = make_workload("decode")
+        extra["decode"] = attn_case(vfa, torch, wd)
+        for page in (16, 128):
+            log(f"[bench] extra: paged decode, {page}-key pages")
+            extra[f"paged_decode_p{page}"] = paged_case(vfa, torch, wd, page)
+        del wd
         log("[bench] extra: attn_update merge")
         extra["attn_update_merge"] = merge_case(vfa, torch)
 

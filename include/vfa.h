@@ -15,13 +15,16 @@
  *     launch error is reported as VFA_ERR_LAUNCH.
  *   - Return values are vfa_status codes (0 = success).
  *   - Debug check: with the environment variable VFA_DEBUG set to anything but
- *     "" or "0" (read on every call), varlen_attn_fwd and
+ *     "" or "0" (read on every call), varlen_attn_fwd, paged_attn_decode and
  *     varlen_last_token_gather first check the cu_seqlens contract on the
  *     device:
  *       - cu[0] == 0;
  *       - entries non-decreasing;
  *       - cu[batch] equals the total (attention only);
- *       - no length above the max_seqlen bound.
+ *       - no length above the max_seqlen bound;
+ *       - paged_attn_decode also: 0 <= seqused_k[b] <= max_seqlen_k, and
+ *         every block-table entry naming a page of those keys lies in
+ *         [0, num_pages).
  *     A violation returns VFA_ERR_SHAPE and launches nothing. The check
  *     synchronises the stream, copies one word to the host and clears a
  *     library word in device memory with hipMemsetAsync. Debug calls must not
@@ -51,7 +54,7 @@
 extern "C" {
 #endif
 
-#define VFA_ABI_VERSION 1
+#define VFA_ABI_VERSION 2
 
 typedef enum vfa_status {
   VFA_OK = 0,
@@ -148,6 +151,64 @@ int32_t varlen_attn_fwd(const void* q, const void* k, const void* v, int32_t in_
 int32_t attn_update(const float* lse, const void* go, int32_t go_dtype,
                     int32_t sp, int64_t bsh, int32_t hd, int32_t update_type,
                     void* out, float* lse_out, void* stream);
+
+/* Bytes of device workspace paged_attn_decode needs for these host sizes
+ * (0 when no sequence can need more than one key split). Same arguments as
+ * varlen_attn_fwd_workspace_size. */
+size_t paged_attn_decode_workspace_size(int32_t batch, int32_t total_q,
+                                        int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                        int32_t num_heads_q, int32_t num_heads_kv,
+                                        int32_t head_dim);
+
+/* Attention of packed queries against a paged K/V cache ([P4] background:
+ * the per-chunk partials its merge combines come from PagedAttention).
+ *
+ * Computes exactly what varlen_attn_fwd computes (same formula, GQA mapping,
+ * bottom-right causal mask, natural-log lse, out = 0 / lse = -inf for a row
+ * with no visible key), with the keys and values of sequence b read from
+ * pages: key j (0 <= j < seqused_k[b]) is slot j % page_size of page
+ * block_table[b, j / page_size] of k_cache and v_cache. The pages give no
+ * cache layout; this is the layout taken.
+ *
+ * q            [total_q, num_heads_q, head_dim]                 bf16
+ * k_cache,
+ * v_cache      [num_pages, page_size, num_heads_kv, head_dim]   bf16
+ * block_table  device int32 [batch, max_pages_per_seq]; only the entries of
+ *              pages holding keys < min(seqused_k[b], max_seqlen_k) are
+ *              read. Entries outside [0, num_pages) are a caller error; they
+ *              are clamped into that range (wrong values, no out-of-range
+ *              read).
+ * cu_seqlens_q device int32 [batch + 1], as in varlen_attn_fwd.
+ * seqused_k    device int32 [batch], keys of each sequence. Keys past the
+ *              host bound max_seqlen_k are ignored (caller error).
+ * max_seqlen_q / max_seqlen_k: host upper bounds, as in varlen_attn_fwd;
+ *              max_seqlen_k <= max_pages_per_seq * page_size is required.
+ * out          [total_q, num_heads_q, head_dim]   out_dtype (bf16 or fp32)
+ * lse          [total_q, num_heads_q]             fp32
+ * workspace / workspace_bytes: device scratch of at least
+ *              paged_attn_decode_workspace_size(...) bytes, 16-byte
+ *              aligned (may be NULL when that size is 0). Its contents on
+ *              entry do not matter. Calls that overlap in time must not
+ *              share a workspace.
+ * Supported: in_dtype bf16; head_dim 64 or 128; page_size a power of two in
+ *              [16, 4096] with page_size * num_heads_kv * head_dim < 2^31;
+ *              any num_heads_q / num_heads_kv. Built for few queries per
+ *              sequence (decode, a few speculative tokens): each group of 16
+ *              (token, head) columns of a kv head reads that sequence's
+ *              keys again, so long query sets belong on varlen_attn_fwd.
+ * batch == 0 or total_q == 0 returns VFA_OK and launches nothing.
+ */
+int32_t paged_attn_decode(const void* q, int32_t in_dtype,
+                          const void* k_cache, const void* v_cache,
+                          const int32_t* block_table, int32_t max_pages_per_seq,
+                          int32_t num_pages, int32_t page_size,
+                          const int32_t* cu_seqlens_q, const int32_t* seqused_k,
+                          int32_t batch, int32_t total_q,
+                          int32_t max_seqlen_q, int32_t max_seqlen_k,
+                          int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                          float softmax_scale, int32_t causal,
+                          void* out, int32_t out_dtype, float* lse,
+                          void* workspace, size_t workspace_bytes, void* stream);
 
 /* Last-token gather ([P1] core optimisation 1, embed(): x[cu_seqlens[1:] - 1]).
  *

@@ -44,7 +44,7 @@ def test_exports_match_header(lib):
 
 
 def test_abi_version(lib):
-    assert lib.vfa_abi_version() == vfa._header_abi_version() == 1
+    assert lib.vfa_abi_version() == vfa._header_abi_version() == 2
 
 
 def test_status_strings(lib):
@@ -156,3 +156,69 @@ def test_workspace_size_plan(lib):
     assert ws(64, 64, 1, 300, 32, 4, 128) == 0                              # short keys: no split
     assert ws(8, 24, 3, 8192, 32, 4, 128) == 0                              # 3 tokens x 8 heads > 16 columns
     assert ws(8, 16, 2, 8192, 16, 2, 64) > 0                                # 2 tokens x 8 heads = 16 columns
+
+
+def _paged(lib, **kw):
+    a = dict(q=P, in_dtype=BF16, kc=P, vc=P, table=P, max_pages=4, num_pages=16, page=16, cu_q=P, used=P,
+             batch=2, total_q=2, max_q=1, max_k=64, hq=32, hkv=4, d=128, scale=0.125, causal=1, out=P,
+             out_dtype=BF16, lse=P, ws=None, ws_bytes=0, stream=None)
+    a.update(kw)
+    return lib.paged_attn_decode(a["q"], a["in_dtype"], a["kc"], a["vc"], a["table"], a["max_pages"],
+                                 a["num_pages"], a["page"], a["cu_q"], a["used"], a["batch"], a["total_q"],
+                                 a["max_q"], a["max_k"], a["hq"], a["hkv"], a["d"], a["scale"], a["causal"],
+                                 a["out"], a["out_dtype"], a["lse"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=0), OK),
+    (dict(total_q=0), OK),
+    (dict(batch=0, q=None), OK),
+    (dict(batch=-1), SHAPE),
+    (dict(max_k=-1), SHAPE),
+    (dict(max_pages=-1), SHAPE),
+    (dict(num_pages=-1), SHAPE),
+    (dict(page=0), SHAPE),
+    (dict(q=None), NULL),
+    (dict(kc=None), NULL),
+    (dict(vc=None), NULL),
+    (dict(table=None), NULL),
+    (dict(cu_q=None), NULL),
+    (dict(used=None), NULL),
+    (dict(out=None), NULL),
+    (dict(lse=None), NULL),
+    (dict(hq=6, hkv=4), SHAPE),
+    (dict(causal=2), SHAPE),
+    (dict(max_q=3), SHAPE),                  # bound above the token count
+    (dict(total_q=3), SHAPE),                # 2 sequences of <= 1 token cannot hold 3
+    (dict(max_k=65), SHAPE),                 # more keys than 4 pages of 16 can hold
+    (dict(num_pages=0), SHAPE),              # keys but no pages
+    (dict(d=96), UNSUP),
+    (dict(in_dtype=F32, out_dtype=F32), UNSUP),
+    (dict(out_dtype=5), UNSUP),
+    (dict(page=8, max_pages=8), UNSUP),      # pages below 16 keys
+    (dict(page=24), UNSUP),                  # not a power of two
+    (dict(page=8192, max_pages=1), UNSUP),
+    (dict(page=4096, max_pages=1, hkv=4096, hq=4096), UNSUP),        # page * hkv * D = 2^31
+    (dict(scale=0.0), UNSUP),
+    (dict(kc=P + 2), UNSUP),
+    (dict(out=P + 8), UNSUP),
+    # long keys need a split workspace
+    (dict(max_k=8192, max_pages=512), WS),
+    (dict(max_k=8192, max_pages=512, ws=P, ws_bytes=16), WS),
+    (dict(max_k=8192, max_pages=512, ws=P + 4, ws_bytes=1 << 30), WS),
+])
+def test_paged_validation(lib, kw, code):
+    assert _paged(lib, **kw) == code
+
+
+def test_paged_workspace_plan(lib):
+    # (sequence, kv head, 16-column group) units set the split length: 4096 keys, halved while fewer than
+    # 2048 (unit, split) pairs; the workspace holds fp32 partial O and lse per split and query row, as on
+    # the contiguous decode path; none when a single split covers max_seqlen_k.
+    ws = lib.paged_attn_decode_workspace_size
+    assert ws(64, 64, 1, 32768, 32, 4, 128) == 8 * 64 * 32 * 129 * 4
+    assert ws(2, 2, 1, 4096, 32, 4, 128) == 16 * 2 * 32 * 129 * 4              # 256-key splits
+    assert ws(2, 6, 3, 4096, 32, 1, 64) == 16 * 6 * 32 * 65 * 4                # 3 tokens x 32 heads = 6 groups
+    assert ws(2, 2, 1, 40000, 32, 1, 64) == 157 * 2 * 32 * 65 * 4              # 2 units: 256-key splits
+    assert ws(64, 64, 1, 256, 32, 4, 128) == 0                                  # one split
+    assert ws(0, 0, 1, 4096, 32, 4, 128) == 0

@@ -14,6 +14,9 @@ Entry points (same names as the C ABI in include/vfa.h):
   attn_update(lse, go, update_type=1) -> (out, lse_out or None)
   varlen_last_token_gather(x, cu_seqlens) -> x[cu_seqlens[1:] - 1]
   varlen_attn_fwd_workspace_size(...) -> bytes
+  paged_attn_decode(q, k_cache, v_cache, block_table, cu_seqlens_q, seqused_k, max_seqlen_q,
+                    max_seqlen_k, softmax_scale=None, causal=True, out_dtype=None) -> (out, lse)
+  paged_attn_decode_workspace_size(...) -> bytes
 """
 from __future__ import annotations
 
@@ -32,6 +35,8 @@ __all__ = [
     "varlen_attn_fwd_workspace_size",
     "attn_update",
     "varlen_last_token_gather",
+    "paged_attn_decode",
+    "paged_attn_decode_workspace_size",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -92,6 +97,19 @@ def load_library() -> ctypes.CDLL:
     lib.varlen_last_token_gather.restype = c.c_int32
     lib.varlen_last_token_gather.argtypes = [c.c_void_p, c.c_int32, c.c_void_p, c.c_int32, c.c_int64,
                                              c.c_void_p, c.c_void_p]
+    lib.paged_attn_decode_workspace_size.restype = c.c_size_t
+    lib.paged_attn_decode_workspace_size.argtypes = [c.c_int32] * 7
+    lib.paged_attn_decode.restype = c.c_int32
+    lib.paged_attn_decode.argtypes = [
+        c.c_void_p, c.c_int32, c.c_void_p, c.c_void_p,          # q in_dtype k_cache v_cache
+        c.c_void_p, c.c_int32, c.c_int32, c.c_int32,            # block_table max_pages num_pages page_size
+        c.c_void_p, c.c_void_p,                                 # cu_q seqused_k
+        c.c_int32, c.c_int32, c.c_int32, c.c_int32,             # batch total_q max_q max_k
+        c.c_int32, c.c_int32, c.c_int32,                        # hq hkv d
+        c.c_float, c.c_int32,                                   # scale causal
+        c.c_void_p, c.c_int32, c.c_void_p,                      # out out_dtype lse
+        c.c_void_p, c.c_size_t, c.c_void_p,                     # workspace bytes stream
+    ]
     got, want = lib.vfa_abi_version(), _header_abi_version()
     if got != want:
         raise RuntimeError(f"{path} has ABI version {got}, include/vfa.h expects {want}: stale library")
@@ -243,3 +261,67 @@ def varlen_last_token_gather(x, cu_seqlens, out=None):
     if st != 0:
         raise VfaError(st, "varlen_last_token_gather")
     return out
+
+
+def paged_attn_decode_workspace_size(batch, total_q, max_seqlen_q, max_seqlen_k, num_heads_q, num_heads_kv,
+                                     head_dim) -> int:
+    return int(load_library().paged_attn_decode_workspace_size(int(batch), int(total_q), int(max_seqlen_q),
+                                                               int(max_seqlen_k), int(num_heads_q),
+                                                               int(num_heads_kv), int(head_dim)))
+
+
+def paged_attn_decode(q, k_cache, v_cache, block_table, cu_seqlens_q, seqused_k, max_seqlen_q: int,
+                      max_seqlen_k: int, softmax_scale: float | None = None, causal: bool = True,
+                      out_dtype=None, out=None, lse=None, workspace=None):
+    """Attention of packed queries against a paged K/V cache. Returns (out [Tq,Hq,D], lse [Tq,Hq] fp32).
+
+    q [Tq, Hq, D] bf16; k_cache / v_cache [num_pages, page_size, Hkv, D] bf16;
+    block_table int32 [B, max_pages]; cu_seqlens_q int32 [B+1]; seqused_k int32
+    [B] (keys of each sequence). max_seqlen_* are host upper bounds. Default
+    scale 1/sqrt(D); default out dtype = bf16.
+    """
+    torch = _torch()
+    lib = load_library()
+    _check_gpu("q", q, 3)
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _check_gpu(name, t, 4)
+    _check_gpu("block_table", block_table, 2)
+    for name, t in (("cu_seqlens_q", cu_seqlens_q), ("seqused_k", seqused_k)):
+        _check_gpu(name, t, 1)
+    for name, t in (("block_table", block_table), ("cu_seqlens_q", cu_seqlens_q), ("seqused_k", seqused_k)):
+        if t.dtype != torch.int32:
+            raise TypeError(f"{name} must be int32")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise TypeError("q, k_cache and v_cache must share one dtype")
+    if k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache and v_cache must have the same shape")
+    if q.shape[2] != k_cache.shape[3]:
+        raise ValueError("q and k_cache must have the same head_dim")
+    tq, hq, d = (int(x) for x in q.shape)
+    num_pages, page_size, hkv = (int(x) for x in k_cache.shape[:3])
+    batch = int(cu_seqlens_q.shape[0]) - 1
+    if int(seqused_k.shape[0]) != batch or int(block_table.shape[0]) != batch:
+        raise ValueError("seqused_k and block_table must have one entry / row per sequence")
+    max_pages = int(block_table.shape[1])
+    in_code = _dtype_code(q)
+    odt = q.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((tq, hq, d), dtype=odt, device=q.device)
+    _check_gpu("out", out, 3)
+    if lse is None:
+        lse = torch.empty((tq, hq), dtype=torch.float32, device=q.device)
+    _check_gpu("lse", lse, 2)
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    ws_bytes = paged_attn_decode_workspace_size(batch, tq, max_seqlen_q, max_seqlen_k, hq, hkv, d)
+    if ws_bytes and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if (ws_bytes and workspace is not None) else None
+    st = lib.paged_attn_decode(q.data_ptr(), in_code, k_cache.data_ptr(), v_cache.data_ptr(),
+                               block_table.data_ptr(), max_pages, num_pages, page_size,
+                               cu_seqlens_q.data_ptr(), seqused_k.data_ptr(),
+                               batch, tq, int(max_seqlen_q), int(max_seqlen_k), hq, hkv, d,
+                               scale, 1 if causal else 0, out.data_ptr(), _dtype_code(out), lse.data_ptr(),
+                               ws_ptr, ws_bytes, _stream_ptr(q.device))
+    if st != 0:
+        raise VfaError(st, "paged_attn_decode")
+    return out, lse

@@ -25,7 +25,7 @@ namespace vfa {
 
 // Split-KV (decode) path: only when the queries of one sequence fit the
 // 16-column tile together with the G heads that share a kv head, and the key
-// sets are long enough for splitting to pay. Keys per split start at 1024
+// sets are long enough for splitting to pay. Keys per split start at 4096
 // and halve (down to 256) until there are enough workgroups to fill the chip.
 DecodePlan plan_decode(int batch, int total_q, int max_seqlen_q, int max_seqlen_k, int hq, int hkv,
                        int head_dim) {
@@ -44,6 +44,24 @@ DecodePlan plan_decode(int batch, int total_q, int max_seqlen_q, int max_seqlen_
   p.chunk = chunk;
   p.n_splits = (max_seqlen_k + chunk - 1) / chunk;
   p.ws_bytes = (size_t)p.n_splits * (size_t)total_q * (size_t)hq * (size_t)(head_dim + 1) * sizeof(float);
+  return p;
+}
+
+// Paged path: the (token, head) columns of a kv head are cut into groups of
+// 16 (one workgroup's MFMA columns); splits follow the same rule as above
+// over (sequence, kv head, column group) units.
+PagedPlan plan_paged(int batch, int total_q, int max_seqlen_q, int max_seqlen_k, int hq, int hkv, int head_dim) {
+  PagedPlan p{256, 1, 1, 0};
+  if (batch <= 0 || total_q <= 0 || max_seqlen_q <= 0 || hq <= 0 || hkv <= 0 || hq % hkv != 0) return p;
+  const long long grp = hq / hkv;
+  p.n_cg = (int)(((long long)max_seqlen_q * grp + 15) / 16);
+  const long long units = (long long)batch * hkv * p.n_cg;
+  int chunk = 4096;
+  while (chunk > 256 && units * ((max_seqlen_k + chunk - 1) / chunk) < 2048) chunk /= 2;
+  p.chunk = chunk;
+  p.n_splits = max_seqlen_k > chunk ? (max_seqlen_k + chunk - 1) / chunk : 1;
+  if (p.n_splits > 1)
+    p.ws_bytes = (size_t)p.n_splits * (size_t)total_q * (size_t)hq * (size_t)(head_dim + 1) * sizeof(float);
   return p;
 }
 
@@ -168,4 +186,62 @@ VFA_API int32_t varlen_last_token_gather(const void* x, int32_t dtype, const int
   return vfa::launch_last_token_gather(x, dtype == VFA_F32 ? 4 : 2, cu_seqlens, batch, row_elems, out, stream) == 0
              ? VFA_OK
              : VFA_ERR_LAUNCH;
+}
+
+VFA_API size_t paged_attn_decode_workspace_size(int32_t batch, int32_t total_q, int32_t max_seqlen_q,
+                                                int32_t max_seqlen_k, int32_t num_heads_q, int32_t num_heads_kv,
+                                                int32_t head_dim) {
+  return vfa::plan_paged(batch, total_q, max_seqlen_q, max_seqlen_k, num_heads_q, num_heads_kv, head_dim).ws_bytes;
+}
+
+VFA_API int32_t paged_attn_decode(const void* q, int32_t in_dtype, const void* k_cache, const void* v_cache,
+                                  const int32_t* block_table, int32_t max_pages_per_seq, int32_t num_pages,
+                                  int32_t page_size, const int32_t* cu_seqlens_q, const int32_t* seqused_k,
+                                  int32_t batch, int32_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                  int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim, float softmax_scale,
+                                  int32_t causal, void* out, int32_t out_dtype, float* lse, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  if (batch < 0 || total_q < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || max_pages_per_seq < 0 || num_pages < 0 ||
+      page_size <= 0)
+    return VFA_ERR_SHAPE;
+  if (batch == 0 || total_q == 0) return VFA_OK;
+  if (!q || !k_cache || !v_cache || !block_table || !cu_seqlens_q || !seqused_k || !out || !lse) return VFA_ERR_NULL;
+  if (num_heads_q <= 0 || num_heads_kv <= 0 || num_heads_q % num_heads_kv != 0) return VFA_ERR_SHAPE;
+  if (causal != 0 && causal != 1) return VFA_ERR_SHAPE;
+  if (max_seqlen_q > total_q || (long long)max_seqlen_q * batch < total_q) return VFA_ERR_SHAPE;
+  if ((long long)max_seqlen_k > (long long)max_pages_per_seq * page_size) return VFA_ERR_SHAPE;
+  if (max_seqlen_k > 0 && num_pages == 0) return VFA_ERR_SHAPE;
+  if (head_dim != 64 && head_dim != 128) return VFA_ERR_UNSUPPORTED;
+  if (in_dtype != VFA_BF16) return VFA_ERR_UNSUPPORTED;
+  if (out_dtype != VFA_F32 && out_dtype != VFA_BF16) return VFA_ERR_UNSUPPORTED;
+  // Page sizes: powers of two from 16 keys (a 32-key step then spans at most two pages) to 4096.
+  if (page_size < 16 || page_size > 4096 || (page_size & (page_size - 1)) != 0) return VFA_ERR_UNSUPPORTED;
+  if ((long long)page_size * num_heads_kv * head_dim >= (1LL << 31)) return VFA_ERR_UNSUPPORTED;
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return VFA_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out)) return VFA_ERR_UNSUPPORTED;
+
+  const vfa::PagedPlan plan =
+      vfa::plan_paged(batch, total_q, max_seqlen_q, max_seqlen_k, num_heads_q, num_heads_kv, head_dim);
+  if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes || !aligned16(workspace)))
+    return VFA_ERR_WORKSPACE;
+
+  if (debug_checks()) {
+    int r = vfa::check_cu_seqlens(cu_seqlens_q, total_q, max_seqlen_q, nullptr, 0, 0, batch, stream);
+    if (r == 0)
+      r = vfa::check_paged(seqused_k, block_table, batch, max_pages_per_seq, page_size, num_pages, max_seqlen_k,
+                           stream);
+    if (r < 0) return VFA_ERR_LAUNCH;
+    if (r > 0) return VFA_ERR_SHAPE;
+  }
+
+  vfa::PagedArgs a{};
+  a.q = q; a.k_cache = k_cache; a.v_cache = v_cache;
+  a.block_table = block_table; a.max_pages = max_pages_per_seq; a.num_pages = num_pages; a.page_size = page_size;
+  a.cu_q = cu_seqlens_q; a.seqused_k = seqused_k;
+  a.batch = batch; a.total_q = total_q; a.max_seqlen_q = max_seqlen_q; a.max_seqlen_k = max_seqlen_k;
+  a.hq = num_heads_q; a.hkv = num_heads_kv; a.grp = num_heads_q / num_heads_kv; a.head_dim = head_dim;
+  a.scale = softmax_scale; a.causal = causal;
+  a.out = out; a.out_dtype = out_dtype == VFA_BF16 ? 1 : 0; a.lse = lse;
+  a.workspace = workspace; a.workspace_bytes = workspace_bytes; a.stream = stream;
+  return vfa::launch_paged_decode_bf16(a, plan) == 0 ? VFA_OK : VFA_ERR_LAUNCH;
 }

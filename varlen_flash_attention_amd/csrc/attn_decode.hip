@@ -1,27 +1,41 @@
 // Split-KV varlen attention for few queries against long key sets (decode), bf16 in.
 //
 // Same result as the prefill kernel (softmax(scale q K^T) V and the natural
-// log-sum-exp per query row, TND layout, cu_seqlens, GQA head h -> h / G,
-// bottom-right causal mask), for the shape where one fused attention op
-// serves incremental decoding ("Qwen3-MoE low-latency inference on Atlas A3",
-// flash attention fused operator section).
+// log-sum-exp per query row, TND queries, GQA head h -> h / G, bottom-right
+// causal mask), for the shape where one fused attention op serves
+// incremental decoding ("Qwen3-MoE low-latency inference on Atlas A3", flash
+// attention fused operator section).
 //
 // Decode reads every K/V byte once and does little arithmetic per byte, so it
 // is bound by HBM bandwidth. Sequence lengths vary widely, so each
 // (sequence, kv head) is cut into fixed-size key chunks ("splits") and the
 // splits become independent workgroups. Each split produces a partial
-// (O_s, lse_s) in the workspace; a combine kernel then merges the splits with
-// the AttentionUpdate rule ("attention_update operator optimisation
-// practice", operator function description) using the same device helpers as
-// the attn_update entry point.
+// (O_s, lse_s); the partials are merged with the AttentionUpdate rule
+// ("attention_update operator optimisation practice", operator function
+// description) using the same device helpers as the attn_update entry point.
+//
+// Two K/V layouts share one kernel template:
+//   contiguous: K/V in TND with cu_seqlens_k. Partials go to a row-indexed
+//               workspace and a combine kernel merges them.
+//   paged:      K/V in fixed-size pages reached through a per-sequence block
+//               table (the PagedAttention operator that page names as the
+//               source of the partials it merges). Queries may exceed the 16
+//               columns of one workgroup: the (token, head) columns of a kv
+//               head are cut into groups of 16. With a single split the split
+//               kernel writes the output itself.
+// In both layouts the partials are merged by a second kernel rather than by
+// the last split to finish: handing partials between workgroups inside one
+// launch needs a device-scope release (an L2 writeback on every XCD) per
+// workgroup, which measured 718 us against 453 us without it at the decode
+// shape.
 //
 // Inside a workgroup (4 waves) every wave owns a strided subset of 32-key
 // steps of the split and keeps its own online-softmax state; the four states
 // are merged through LDS at the end. The G query heads of the kv head (times
-// up to 16 / G query tokens) fill the 16 columns of v_mfma_f32_16x16x32_bf16:
-//   S^T = K Q^T   : A = K rows loaded straight from global memory (16 B per
-//                   lane), B = Q^T in registers.
-//   O^T += V^T P^T: V rows go through a wave-private LDS buffer so that
+// the query tokens) fill the 16 columns of v_mfma_f32_16x16x32_bf16:
+//   S^T = K Q^T   : A = K rows parked in a wave-private LDS buffer and read
+//                   back 16 B per lane, B = Q^T in registers.
+//   O^T += V^T P^T: V rows go through the same buffer so that
 //                   ds_read_b64_tr_b16 can deliver V^T; B = P^T from registers.
 #include "common.h"
 #include "launch.h"
@@ -33,6 +47,31 @@ constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kCols = 16;      // query columns (heads x tokens) per workgroup
 constexpr int kStep = 32;      // keys per wave step
+// Paged K/V: the page ids of one split are staged in LDS. A split holds at
+// most kMaxChunk keys and a page at least kMinPage keys (so a 32-key step
+// touches at most two pages).
+constexpr int kMaxChunk = 4096;
+constexpr int kMinPage = 16;
+constexpr int kPageSlots = kMaxChunk / kMinPage;
+
+// Kernel arguments of the split kernel (contiguous or paged K/V).
+struct SplitArgs {
+  const bf16* q;                // [total_q, hq, D]
+  const bf16* k;                // contiguous: [total_k, hkv, D]; paged: [num_pages, 2^lg_page, hkv, D]
+  const bf16* v;
+  const int32_t* cu_q;          // [batch + 1]
+  const int32_t* cu_k;          // contiguous: [batch + 1]
+  const int32_t* seqused_k;     // paged: keys of each sequence [batch]
+  const int32_t* block_table;   // paged: [batch, max_pages]
+  int batch, hq, hkv, grp, chunk, n_splits;
+  int max_pages, num_pages, lg_page, max_seqlen_k, n_cg;
+  long long rows_total;         // total_q * hq (row-indexed partials)
+  float scale, scale_log2;
+  float* ws_o;                  // partial O [n_splits][rows_total][D]
+  float* ws_lse;                // partial lse [n_splits][rows_total]
+  void* out;                    // paged with one split: final [total_q, hq, D]
+  float* lse;                   // paged with one split: final [total_q, hq]
+};
 
 template <int D>
 struct DSmem {
@@ -54,32 +93,68 @@ __device__ __forceinline__ bf16x8 tr_pair(const char VFA_LDS* p0, const char VFA
   return __builtin_bit_cast(bf16x8, r);
 }
 
-// Grid: n_splits * batch * hkv workgroups. Partials go to
-// ws_o[split][row][D] and ws_lse[split][row], row = token * hq + head.
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void attn_decode_split_kernel(
-    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int batch, int hq, int hkv,
-    int grp, int chunk, int n_splits, long long rows_total, float scale, float scale_log2,
-    float* __restrict__ ws_o, float* __restrict__ ws_lse) {
+// Writes one column slice of a final output row: O (D / 16 values from md on)
+// and, from the column's first thread, its lse.
+template <int D, typename OutT>
+__device__ __forceinline__ void store_row(void* out, float* lse, long long row, int md, bool lead,
+                                          const f32x4 (&o)[D / 64], float lse_v) {
+  OutT* dst = (OutT*)out + row * D + md;
+#pragma unroll
+  for (int x = 0; x < D / 64; ++x)
+#pragma unroll
+    for (int y = 0; y < 4; ++y) dst[x * 4 + y] = from_f32<OutT>(o[x][y]);
+  if (lead) lse[row] = lse_v;
+}
+
+// Grid, contiguous: n_splits * batch * hkv workgroups. Grid, paged:
+// n_splits * batch * hkv * n_cg workgroups (column group fastest). Partials
+// go to ws_o[split][row][D] and ws_lse[split][row], row = token * hq + head;
+// paged with n_splits == 1 writes out and lse instead.
+template <int D, bool CAUSAL, bool PAGED, typename OutT>
+__global__ __launch_bounds__(kThreads, 2) void attn_decode_split_kernel(const SplitArgs p) {
   using S = DSmem<D>;
   __shared__ __attribute__((aligned(16))) char smem[S::TOTAL];
+  __shared__ int pages[PAGED ? kPageSlots : 1];
   char VFA_LDS* lds = (char VFA_LDS*)smem;
 
   // Longest splits first: split index descends with the block id.
-  const int per_s = batch * hkv;
-  const int split = n_splits - 1 - (int)(blockIdx.x / per_s);
-  const int bg = blockIdx.x % per_s;
-  const int b = bg / hkv;
-  const int g = bg % hkv;
+  const int per_s = p.batch * p.hkv;
+  int split, b, g, cg = 0;
+  if constexpr (PAGED) {
+    cg = (int)(blockIdx.x % p.n_cg);
+    const int r = (int)(blockIdx.x / p.n_cg);
+    split = p.n_splits - 1 - r / per_s;
+    b = (r % per_s) / p.hkv;
+    g = r % p.hkv;
+  } else {
+    split = p.n_splits - 1 - (int)(blockIdx.x / per_s);
+    const int bg = blockIdx.x % per_s;
+    b = bg / p.hkv;
+    g = bg % p.hkv;
+  }
+  const int grp = p.grp;
+  const float scale_log2 = p.scale_log2;
 
-  const int q0 = cu_q[b];
-  const int lq = cu_q[b + 1] - q0;
-  const int k0 = cu_k[b];
-  const int lk = cu_k[b + 1] - k0;
-  const int key_lo = split * chunk;
-  if (lq <= 0 || key_lo >= lk) return;     // this split holds no key of the sequence
-  const int key_hi = min(lk, key_lo + chunk);
+  const int q0 = p.cu_q[b];
+  const int lq = p.cu_q[b + 1] - q0;
+  int k0 = 0, lk;
+  if constexpr (PAGED) {
+    // Keys past the host bound are ignored, so the block table is never read
+    // past max_seqlen_k / page_size entries.
+    lk = min(max(p.seqused_k[b], 0), p.max_seqlen_k);
+  } else {
+    k0 = p.cu_k[b];
+    lk = p.cu_k[b + 1] - k0;
+  }
+  const int key_lo = split * p.chunk;
+  if constexpr (PAGED) {
+    if (lq * grp <= cg * kCols) return;                  // no (token, head) column in this group
+    // A sequence without keys still owes its rows out = 0, lse = -inf; split 0 writes them.
+    if (key_lo >= lk && !(lk == 0 && split == 0)) return;
+  } else {
+    if (lq <= 0 || key_lo >= lk) return;                 // this split holds no key of the sequence
+  }
+  const int key_hi = min(lk, key_lo + p.chunk);
   const int diag = lk - lq;
 
   const int tid = threadIdx.x;
@@ -89,22 +164,43 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decode_split_kernel(
   const int grp4 = lane >> 4;
 
   // Column -> (token, head): tokens outer, the G heads of this kv head inner.
-  const int tpc = kCols / grp;                 // tokens per workgroup (>= 1)
-  const bool colvalid = c16 < tpc * grp;
-  const int tq = colvalid ? c16 / grp : 0;
-  const int head = g * grp + (colvalid ? c16 % grp : 0);
-  const bool qvalid = colvalid && tq < lq;
+  int tq, head;
+  bool qvalid;
+  if constexpr (PAGED) {
+    const int col = cg * kCols + c16;
+    tq = col / grp;
+    head = g * grp + col % grp;
+    qvalid = tq < lq;
+  } else {
+    const int tpc = kCols / grp;                         // tokens per workgroup (>= 1)
+    const bool colvalid = c16 < tpc * grp;
+    tq = colvalid ? c16 / grp : 0;
+    head = g * grp + (colvalid ? c16 % grp : 0);
+    qvalid = colvalid && tq < lq;
+  }
 
   // Q^T (B operand): column c16, k-slot grp4*8 + e <-> d = ks*32 + grp4*8 + e.
   bf16x8 qreg[D / 32];
   {
-    const bf16* qrow = q + ((size_t)(q0 + (qvalid ? tq : 0)) * hq + head) * D + grp4 * 8;
+    const bf16* qrow = p.q + ((size_t)(q0 + (qvalid ? tq : 0)) * p.hq + head) * D + grp4 * 8;
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) {
       bf16x8 t = *(const bf16x8*)(qrow + ks * 32);
       if (!qvalid) t = bf16x8{};
       qreg[ks] = t;
     }
+  }
+
+  // Paged: the split's page ids, clamped to the cache so that a bad table
+  // entry cannot send a load outside it.
+  int lg = 0, pbase = 0;
+  if constexpr (PAGED) {
+    lg = p.lg_page;
+    pbase = key_lo >> lg;
+    const int npg = key_hi > key_lo ? ((key_hi - 1) >> lg) - pbase + 1 : 0;   // <= kPageSlots
+    const int32_t* trow = p.block_table + (long long)b * p.max_pages + pbase;
+    for (int i = tid; i < npg; i += kThreads) pages[i] = (int)min((unsigned)trow[i], (unsigned)(p.num_pages - 1));
+    __syncthreads();
   }
 
   f32x4 acc[D / 16];
@@ -124,25 +220,44 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decode_split_kernel(
   typedef u32x4 VRegs[S::VREGS];
   KRegs kA, kB;
   VRegs vA, vB;
-  const bf16* kg = k + ((size_t)k0 * hkv + g) * D;
-  const bf16* vg = v + ((size_t)k0 * hkv + g) * D;
-  const size_t kv_stride = (size_t)hkv * D;
+  const size_t kv_stride = (size_t)p.hkv * D;
+  const bf16* kg = p.k + ((size_t)k0 * p.hkv + g) * D;
+  const bf16* vg = p.v + ((size_t)k0 * p.hkv + g) * D;
   // K and V rows are loaded whole (each instruction covers 64 / (D/8) rows of
   // contiguous bytes) and parked in the wave's LDS buffers.
   auto gload = [&](KRegs& kr, VRegs& vr, int st) {
     const int base = key_lo + st * kStep;
+    if constexpr (PAGED) {
+      // Steps start at multiples of 32 and pages hold a power of two >= 16
+      // keys, so keys 0-15 of a step lie in the page of `base` and keys 16-31
+      // (clamped to the last key) in the page of min(base + 16, last key).
+      const size_t page_elems = kv_stride << lg;
+      const size_t lo_off = (size_t)pages[(base >> lg) - pbase] * page_elems;
+      const size_t hi_off = (size_t)pages[(min(base + 16, key_hi - 1) >> lg) - pbase] * page_elems;
+      const int in_page = (1 << lg) - 1;
 #pragma unroll
-    for (int i = 0; i < S::VREGS; ++i) {
-      const int f = i * 64 + lane;
-      const int key = min(base + f / (D / 8), key_hi - 1);
-      const size_t off = (size_t)key * kv_stride + (f % (D / 8)) * 8;
-      // Streaming loads: every K/V byte is read once (measured 9% faster on
-      // MI355X at the decode shape than plain loads).
-      kr[i] = __builtin_nontemporal_load((const u32x4*)(kg + off));
-      vr[i] = __builtin_nontemporal_load((const u32x4*)(vg + off));
+      for (int i = 0; i < S::VREGS; ++i) {
+        const int f = i * 64 + lane;
+        const int key = min(base + f / (D / 8), key_hi - 1);
+        // In-page offset: fits 32 bits (page_size * hkv * D < 2^31, checked on the host).
+        const uint32_t off = (uint32_t)(key & in_page) * (uint32_t)kv_stride + (f % (D / 8)) * 8;
+        const size_t pg = (i * (64 / (D / 8)) < 16) ? lo_off : hi_off;
+        kr[i] = __builtin_nontemporal_load((const u32x4*)(kg + pg + off));
+        vr[i] = __builtin_nontemporal_load((const u32x4*)(vg + pg + off));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < S::VREGS; ++i) {
+        const int f = i * 64 + lane;
+        const int key = min(base + f / (D / 8), key_hi - 1);
+        const size_t off = (size_t)key * kv_stride + (f % (D / 8)) * 8;
+        // Streaming loads: every K/V byte is read once (measured 9% faster on
+        // MI355X at the decode shape than plain loads).
+        kr[i] = __builtin_nontemporal_load((const u32x4*)(kg + off));
+        vr[i] = __builtin_nontemporal_load((const u32x4*)(vg + off));
+      }
     }
   };
-
   const int tr_i = lane & 15;
   const int tr_key = grp4 * 4 + (tr_i >> 2);
   const int tr_d = 4 * (tr_i & 3);
@@ -250,7 +365,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decode_split_kernel(
   float VFA_LDS* m_lse = (float VFA_LDS*)lds;                       // [kWaves][kCols]
   float VFA_LDS* m_o = m_lse + kWaves * kCols;                      // [kWaves][kCols][D]
   if (grp4 == 0)
-    m_lse[wave * kCols + c16] = l_tot > 0.f ? m_run * scale + fast_log2(l_tot) * kLn2 : neg_inf();
+    m_lse[wave * kCols + c16] = l_tot > 0.f ? m_run * p.scale + fast_log2(l_tot) * kLn2 : neg_inf();
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
 #pragma unroll
   for (int db = 0; db < D / 16; ++db)
@@ -261,24 +376,38 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decode_split_kernel(
   // 256 threads = 16 columns x 16 threads; each thread merges D/16 values of one column.
   const int mc = tid >> 4;
   const int md = (tid & 15) * (D / 16);
-  const bool mvalid = mc < tpc * grp && (mc / grp) < lq;
+  int colm;
+  bool mvalid;
+  if constexpr (PAGED) {
+    colm = cg * kCols + mc;
+    mvalid = colm < lq * grp;
+  } else {
+    colm = mc;
+    mvalid = mc < (kCols / grp) * grp && (mc / grp) < lq;
+  }
   if (!mvalid) return;
   float lw[kWaves], w[kWaves];
 #pragma unroll
   for (int i = 0; i < kWaves; ++i) lw[i] = m_lse[i * kCols + mc];
   const float lse_m = merge_weights<kWaves>(lw, kWaves, w);
-  const long long row = (long long)(q0 + mc / grp) * hq + g * grp + (mc % grp);
-  float* dst = ws_o + ((long long)split * rows_total + row) * D + md;
+  f32x4 o[D / 64];
 #pragma unroll
-  for (int x = 0; x < D / 16; x += 4) {
-    f32x4 o = f32x4{};
+  for (int x = 0; x < D / 64; ++x) {
+    o[x] = f32x4{};
 #pragma unroll
     for (int i = 0; i < kWaves; ++i)
 #pragma unroll
-      for (int y = 0; y < 4; ++y) o[y] += w[i] * m_o[(i * kCols + mc) * D + md + x + y];
-    *(f32x4*)(dst + x) = o;
+      for (int y = 0; y < 4; ++y) o[x][y] += w[i] * m_o[(i * kCols + mc) * D + md + x * 4 + y];
   }
-  if ((tid & 15) == 0) ws_lse[(long long)split * rows_total + row] = lse_m;
+  const long long row = (long long)(q0 + colm / grp) * p.hq + g * grp + colm % grp;
+  if (PAGED && p.n_splits == 1) {                                  // the only split: final result
+    store_row<D, OutT>(p.out, p.lse, row, md, (tid & 15) == 0, o, lse_m);
+    return;
+  }
+  float* dst = p.ws_o + ((long long)split * p.rows_total + row) * D + md;
+#pragma unroll
+  for (int x = 0; x < D / 64; ++x) *(f32x4*)(dst + x * 4) = o[x];
+  if ((tid & 15) == 0) p.ws_lse[(long long)split * p.rows_total + row] = lse_m;
 }
 
 // Merge the splits of every row with the AttentionUpdate rule. Grid: (row
@@ -288,9 +417,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decode_split_kernel(
 // for very long key sets).
 template <int D, int NS, typename OutT>
 __global__ __launch_bounds__(256) void attn_decode_combine_kernel(
-    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int hq, int chunk, int n_splits,
-    long long rows_total, const float* __restrict__ ws_o, const float* __restrict__ ws_lse,
-    OutT* __restrict__ out, float* __restrict__ lse) {
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, const int32_t* __restrict__ seqused_k,
+    int max_seqlen_k, int hq, int chunk, int n_splits, long long rows_total, const float* __restrict__ ws_o,
+    const float* __restrict__ ws_lse, OutT* __restrict__ out, float* __restrict__ lse) {
   constexpr int TPR = D / 4;
   constexpr int RPB = 256 / TPR;
   const int b = blockIdx.y;
@@ -300,7 +429,9 @@ __global__ __launch_bounds__(256) void attn_decode_combine_kernel(
   if (r_in >= rows_b) return;
   const long long row = (long long)q0 * hq + r_in;
   const int c4 = (threadIdx.x % TPR) * 4;
-  const int lk = cu_k[b + 1] - cu_k[b];
+  // Keys of the sequence: from cu_seqlens_k, or (paged) from seqused_k clamped
+  // as the split kernel clamps it.
+  const int lk = seqused_k ? min(max(seqused_k[b], 0), max_seqlen_k) : cu_k[b + 1] - cu_k[b];
   // Splits written for this sequence (keys past a too-small max_seqlen_k bound
   // were never split: the count is capped at the workspace's split count).
   const int n = lk > 0 ? min((lk + chunk - 1) / chunk, n_splits) : 0;
@@ -338,16 +469,18 @@ __global__ __launch_bounds__(256) void attn_decode_combine_kernel(
   if (c4 == 0) lse[row] = lse_m;
 }
 
+// Combine launch shared by both layouts (seqused_k == NULL: contiguous).
 template <int D, typename OutT>
-void launch_combine(const AttnArgs& a, const DecodePlan& p, long long rows, const float* ws_o,
-                    const float* ws_lse) {
+void launch_combine(const int32_t* cu_q, const int32_t* cu_k, const int32_t* seqused_k, int max_seqlen_k,
+                    int batch, int max_seqlen_q, int hq, const DecodePlan& p, long long rows, const float* ws_o,
+                    const float* ws_lse, void* out, float* lse, void* stream) {
   constexpr int RPB = 256 / (D / 4);
-  const long long max_rows = (long long)a.max_seqlen_q * a.hq;
-  const dim3 grid((unsigned)((max_rows + RPB - 1) / RPB), (unsigned)a.batch);
-  hipStream_t st = (hipStream_t)a.stream;
+  const long long max_rows = (long long)max_seqlen_q * hq;
+  const dim3 grid((unsigned)((max_rows + RPB - 1) / RPB), (unsigned)batch);
+  hipStream_t st = (hipStream_t)stream;
 #define VFA_COMBINE(NS)                                                                                    \
-  hipLaunchKernelGGL((attn_decode_combine_kernel<D, NS, OutT>), grid, dim3(256), 0, st, a.cu_q, a.cu_k, a.hq, \
-                     p.chunk, p.n_splits, rows, ws_o, ws_lse, (OutT*)a.out, a.lse)
+  hipLaunchKernelGGL((attn_decode_combine_kernel<D, NS, OutT>), grid, dim3(256), 0, st, cu_q, cu_k, seqused_k, \
+                     max_seqlen_k, hq, p.chunk, p.n_splits, rows, ws_o, ws_lse, (OutT*)out, lse)
   if (p.n_splits <= 8) VFA_COMBINE(8);
   else if (p.n_splits <= 16) VFA_COMBINE(16);
   else if (p.n_splits <= 32) VFA_COMBINE(32);
@@ -363,12 +496,49 @@ int launch_t(const AttnArgs& a, const DecodePlan& p) {
   float* ws_lse = ws_o + (size_t)p.n_splits * rows * D;
   const long long blocks = (long long)p.n_splits * a.batch * a.hkv;
   if (blocks > 0x7fffffffLL) return -1;
-  hipLaunchKernelGGL((attn_decode_split_kernel<D, CAUSAL>), dim3((unsigned)blocks), dim3(kThreads), 0,
-                     (hipStream_t)a.stream, (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.cu_q,
-                     a.cu_k, a.batch, a.hq, a.hkv, a.grp, p.chunk, p.n_splits, rows, a.scale,
-                     a.scale * kLog2e, ws_o, ws_lse);
+  SplitArgs s{};
+  s.q = (const bf16*)a.q; s.k = (const bf16*)a.k; s.v = (const bf16*)a.v;
+  s.cu_q = a.cu_q; s.cu_k = a.cu_k;
+  s.batch = a.batch; s.hq = a.hq; s.hkv = a.hkv; s.grp = a.grp; s.chunk = p.chunk; s.n_splits = p.n_splits;
+  s.n_cg = 1; s.rows_total = rows;
+  s.scale = a.scale; s.scale_log2 = a.scale * kLog2e;
+  s.ws_o = ws_o; s.ws_lse = ws_lse;
+  hipLaunchKernelGGL((attn_decode_split_kernel<D, CAUSAL, false, float>), dim3((unsigned)blocks), dim3(kThreads),
+                     0, (hipStream_t)a.stream, s);
   if (hipGetLastError() != hipSuccess) return -1;
-  launch_combine<D, OutT>(a, p, rows, ws_o, ws_lse);
+  launch_combine<D, OutT>(a.cu_q, a.cu_k, nullptr, a.max_seqlen_k, a.batch, a.max_seqlen_q, a.hq, p, rows, ws_o,
+                          ws_lse, a.out, a.lse, a.stream);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+template <int D, bool CAUSAL, typename OutT>
+int launch_paged_t(const PagedArgs& a, const PagedPlan& p) {
+  if (p.chunk > kMaxChunk || a.page_size < kMinPage) return -1;
+  const long long blocks = (long long)p.n_splits * a.batch * a.hkv * p.n_cg;
+  if (blocks > 0x7fffffffLL) return -1;
+  const long long rows = (long long)a.total_q * a.hq;
+  SplitArgs s{};
+  s.q = (const bf16*)a.q; s.k = (const bf16*)a.k_cache; s.v = (const bf16*)a.v_cache;
+  s.cu_q = a.cu_q; s.seqused_k = a.seqused_k; s.block_table = a.block_table;
+  s.batch = a.batch; s.hq = a.hq; s.hkv = a.hkv; s.grp = a.grp; s.chunk = p.chunk; s.n_splits = p.n_splits;
+  s.max_pages = a.max_pages; s.num_pages = a.num_pages; s.max_seqlen_k = a.max_seqlen_k; s.n_cg = p.n_cg;
+  s.lg_page = 0;
+  while ((1 << s.lg_page) < a.page_size) ++s.lg_page;
+  s.rows_total = rows;
+  s.scale = a.scale; s.scale_log2 = a.scale * kLog2e;
+  s.out = a.out; s.lse = a.lse;
+  if (p.n_splits > 1) {
+    s.ws_o = (float*)a.workspace;
+    s.ws_lse = s.ws_o + (size_t)p.n_splits * rows * D;
+  }
+  hipLaunchKernelGGL((attn_decode_split_kernel<D, CAUSAL, true, OutT>), dim3((unsigned)blocks), dim3(kThreads),
+                     0, (hipStream_t)a.stream, s);
+  if (hipGetLastError() != hipSuccess) return -1;
+  if (p.n_splits > 1) {
+    const DecodePlan dp{true, p.chunk, p.n_splits, p.ws_bytes};
+    launch_combine<D, OutT>(a.cu_q, nullptr, a.seqused_k, a.max_seqlen_k, a.batch, a.max_seqlen_q, a.hq, dp, rows,
+                            s.ws_o, s.ws_lse, a.out, a.lse, a.stream);
+  }
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
@@ -382,6 +552,16 @@ int launch_attn_decode_bf16(const AttnArgs& a, const DecodePlan& p) {
   }
   if (a.causal) return f32out ? launch_t<64, true, float>(a, p) : launch_t<64, true, bf16>(a, p);
   return f32out ? launch_t<64, false, float>(a, p) : launch_t<64, false, bf16>(a, p);
+}
+
+int launch_paged_decode_bf16(const PagedArgs& a, const PagedPlan& p) {
+  const bool f32out = a.out_dtype == 0;
+  if (a.head_dim == 128) {
+    if (a.causal) return f32out ? launch_paged_t<128, true, float>(a, p) : launch_paged_t<128, true, bf16>(a, p);
+    return f32out ? launch_paged_t<128, false, float>(a, p) : launch_paged_t<128, false, bf16>(a, p);
+  }
+  if (a.causal) return f32out ? launch_paged_t<64, true, float>(a, p) : launch_paged_t<64, true, bf16>(a, p);
+  return f32out ? launch_paged_t<64, false, float>(a, p) : launch_paged_t<64, false, bf16>(a, p);
 }
 
 }  // namespace vfa

@@ -35,10 +35,43 @@ struct DecodePlan {
 DecodePlan plan_decode(int batch, int total_q, int max_seqlen_q, int max_seqlen_k, int hq, int hkv,
                        int head_dim);
 
+// Paged K/V (decode-shaped): caches [num_pages, page_size, hkv, D], block
+// table [batch, max_pages], keys per sequence in seqused_k.
+struct PagedArgs {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_table;
+  int max_pages, num_pages, page_size;
+  const int32_t* cu_q;
+  const int32_t* seqused_k;
+  int batch, total_q, max_seqlen_q, max_seqlen_k;
+  int hq, hkv, grp, head_dim;
+  float scale;
+  int causal;
+  void* out;
+  int out_dtype;  // 0 = fp32, 1 = bf16
+  float* lse;
+  void* workspace;
+  size_t workspace_bytes;
+  void* stream;
+};
+
+// Split plan of the paged path: (token, head) columns of a kv head in n_cg
+// groups of 16, keys per split, splits at max_seqlen_k.
+struct PagedPlan {
+  int chunk;
+  int n_splits;
+  int n_cg;
+  size_t ws_bytes;   // partial O + partial lse (fp32) per split and row; 0 with one split
+};
+PagedPlan plan_paged(int batch, int total_q, int max_seqlen_q, int max_seqlen_k, int hq, int hkv, int head_dim);
+
 // Each returns 0 on success, -1 if the HIP runtime reported a launch error.
 int launch_attn_fwd_bf16(const AttnArgs& a);
 int launch_attn_decode_bf16(const AttnArgs& a, const DecodePlan& plan);
 int launch_attn_fwd_f32(const AttnArgs& a);
+int launch_paged_decode_bf16(const PagedArgs& a, const PagedPlan& plan);
 int launch_attn_update(const float* lse, const void* go, int go_dtype, int sp, int64_t bsh, int hd,
                        int update_type, void* out, float* lse_out, void* stream);
 int launch_last_token_gather(const void* x, int esize, const int32_t* cu, int batch, int64_t row_elems,
@@ -50,5 +83,11 @@ int launch_last_token_gather(const void* x, int esize, const int32_t* cu, int ba
 // error.
 int check_cu_seqlens(const int32_t* cu_a, int total_a, int max_a, const int32_t* cu_b, int total_b, int max_b,
                      int batch, void* stream);
+
+// Caller-contract check of the paged inputs: 0 <= seqused_k[b] <= max_seqlen_k
+// and every block-table entry that names one of those keys' pages lies in
+// [0, num_pages). Synchronises the stream; same return values.
+int check_paged(const int32_t* seqused_k, const int32_t* block_table, int batch, int max_pages, int page_size,
+                int num_pages, int max_seqlen_k, void* stream);
 
 }  // namespace vfa

@@ -37,6 +37,8 @@ __all__ = [
     "make_workload",
     "make_custom",
     "chunk_bounds",
+    "PagedCache",
+    "make_paged",
     "WORKLOAD_NAMES",
 ]
 
@@ -263,3 +265,70 @@ def chunk_bounds(length: int, sp: int) -> list[tuple[int, int]]:
     divides L, otherwise sizes differ by at most one.
     """
     return [((c * length) // sp, ((c + 1) * length) // sp) for c in range(sp)]
+
+
+@dataclass
+class PagedCache:
+    """A workload's K/V laid out in fixed-size pages behind a per-sequence block table."""
+    page_size: int
+    k_cache: np.ndarray = field(repr=False)      # fp32 values [num_pages, page_size, Hkv, D]
+    v_cache: np.ndarray = field(repr=False)
+    block_table: np.ndarray = field(repr=False)  # int32 [B, max_pages]; -1 past a sequence's pages
+    seqused_k: np.ndarray = field(repr=False)    # int32 [B], keys of each sequence
+
+    @property
+    def num_pages(self) -> int:
+        return int(self.k_cache.shape[0])
+
+    @property
+    def max_pages(self) -> int:
+        return int(self.block_table.shape[1])
+
+
+def make_paged(w: Workload, page_size: int, seed: int = 0, spare_pages: int = 3) -> PagedCache:
+    """Write the workload's K and V into a paged cache.
+
+    Layout (the reading taken for a PagedAttention cache, whose layout the
+    pages do not give): key j of sequence b sits in slot j % page_size of
+    page block_table[b, j // page_size]. Logical pages go to physical pages
+    in a seeded random order, so consecutive pages of a sequence are
+    scattered; slots past a sequence's last key and ``spare_pages`` unused
+    pages hold other N(0,1) draws (bf16-rounded for bf16 workloads), so a
+    read from a wrong page or slot changes the result.
+    """
+    if page_size < 1:
+        raise ValueError("page_size must be positive")
+    lk = w.lengths_k.astype(np.int64)
+    need = (lk + page_size - 1) // page_size
+    num_pages = int(need.sum()) + int(spare_pages)
+    max_pages = max(int(need.max()) if len(need) else 0, 1)
+    s_perm, s_k, s_v = np.random.SeedSequence([int(seed), int(page_size)]).spawn(3)
+    perm = np.random.default_rng(s_perm).permutation(num_pages)
+    shape = (num_pages, page_size, w.num_heads_kv, w.head_dim)
+    k_cache = np.empty(shape, dtype=np.float32)
+    v_cache = np.empty(shape, dtype=np.float32)
+    filled = np.zeros((num_pages, page_size), dtype=bool)
+    table = np.full((w.batch, max_pages), -1, dtype=np.int32)
+    cu = w.cu_seqlens_k.astype(np.int64)
+    nxt = 0
+    for b in range(w.batch):
+        phys = perm[nxt:nxt + need[b]]
+        nxt += int(need[b])
+        table[b, :need[b]] = phys
+        n = int(lk[b])
+        full, rem = n // page_size, n % page_size
+        for cache, src in ((k_cache, w.k), (v_cache, w.v)):
+            rows = src[cu[b]:cu[b + 1]]
+            if full:            # whole pages: key j -> page phys[j // page_size], slot j % page_size
+                cache[phys[:full]] = rows[:full * page_size].reshape(full, page_size, *rows.shape[1:])
+            if rem:
+                cache[phys[full], :rem] = rows[full * page_size:]
+        filled[phys[:full]] = True
+        if rem:
+            filled[phys[full], :rem] = True
+    n_free = int((~filled).sum())
+    for cache, ss in ((k_cache, s_k), (v_cache, s_v)):
+        junk = _normal(ss, (n_free, w.num_heads_kv, w.head_dim))
+        cache[~filled] = round_to_bf16(junk, inplace=True) if w.dtype == "bf16" else junk
+    return PagedCache(page_size=int(page_size), k_cache=k_cache, v_cache=v_cache, block_table=table,
+                      seqused_k=lk.astype(np.int32))
