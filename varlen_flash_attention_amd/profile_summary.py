@@ -54,6 +54,8 @@ def main(src, dst):
     lines += ["",
               "kernel name key: attn_fwd_bf16_kernel<WAVES, NQ, D, CAUSAL, OutT>; ILi8ELi1ELi128ELb1 = 8 waves of "
               "32 query columns, D=128, causal.",
+              "  attn_decode_split_kernel<D, CAUSAL, PAGED, OutT>: ILi128ELb1ELb0 = contiguous decode (bench extra "
+              "'decode'), ILi128ELb1ELb1 = paged decode (extras 'paged_decode_p16' and '_p128', one row for both).",
               f"headline kernel: {len(head_us)} launches = {warmup} warm-up + {steps} timed + the later extras' "
               "launches of the same kernel (none).",
               f"agreement: the {steps} timed launches average {trace_avg:.1f} us in this trace; bench.py's HIP events "
