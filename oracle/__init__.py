@@ -9,7 +9,10 @@ Parity status per function (what pins it; see tests/test_oracle_*.py):
       math.fsum on tiny cases, torch CPU fp64 scaled_dot_product_attention on
       padded per-sequence inputs, closed forms (Q = 0, causal row 0, constant
       V, single key) and invariants (packing, GQA = MHA on repeated K/V,
-      key shift, scale folding, lse bounds, sequence permutation).
+      key shift, scale folding, lse bounds, sequence permutation). The
+      causal_offset option: brute force with offsets, and a key chunk
+      computed alone with offset -a equals the chunked partial that keeps
+      absolute positions through key_range.
   attn_update -- pinned: hand-worked golden values, chunked + merged equals
       unchunked attention, sp = 1 identity, chunk permutation, -inf chunks.
   chunked_partials -- pinned through the chunked + merged == unchunked check.

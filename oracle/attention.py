@@ -34,7 +34,10 @@ Readings where the pages are silent (each also listed in the design notes):
     repeat_interleave(G, dim=1) produces ([P1] core optimisation 5).
   * Causal mask when Lq != Lk: aligned bottom-right, query i sees key j iff
     j <= i + (Lk - Lq). With Lq == Lk this is exactly [P1] 2.1's
-    triu(ones, diagonal=1) == masked.
+    triu(ones, diagonal=1) == masked. An explicit per-sequence offset may
+    replace Lk - Lq: it is the position of the sequence's first query minus
+    that of its first key, which is how a key chunk [a, c) of a sequence
+    ([P4]'s sequence-parallel chunks) keeps the absolute mask: offset -a.
   * lse is the natural log of sum_j exp(scale * q.k_j) over visible keys
     ([P4]: "log-sum-exp, the normalisation factor of the attention weights").
   * A row with no visible key: lse = -inf and O = 0. The merge ignores
@@ -68,17 +71,20 @@ def _as64(x) -> np.ndarray:
     return np.asarray(x, dtype=np.float64)
 
 
-def _visible(i_pos: np.ndarray, lq: int, lk: int, causal: bool, key_lo: int, key_hi: int) -> np.ndarray:
+def _visible(i_pos: np.ndarray, lq: int, lk: int, causal: bool, key_lo: int, key_hi: int,
+             offset=None) -> np.ndarray:
     """Boolean [n, key_hi-key_lo]: key j (absolute in the sequence) is visible to query i.
 
     [P1] 2.1: the causal mask is triu(ones, diagonal=1) with True = masked,
     i.e. key j is hidden from query i when j > i. Bottom-right alignment
-    shifts that by Lk - Lq.
+    shifts that by Lk - Lq; an explicit offset (first query's position minus
+    first key's position) replaces Lk - Lq.
     """
     j = np.arange(key_lo, key_hi, dtype=np.int64)[None, :]
     vis = np.ones((len(i_pos), key_hi - key_lo), dtype=bool)
     if causal:
-        vis &= j <= (i_pos[:, None] + (lk - lq))
+        off = (lk - lq) if offset is None else int(offset)
+        vis &= j <= (i_pos[:, None] + off)
     return vis
 
 
@@ -110,14 +116,16 @@ def _attend_rows(q_rows: np.ndarray, k_seq: np.ndarray, v_seq: np.ndarray, scale
 
 
 def varlen_attention_rows(q, k, v, cu_seqlens_q, cu_seqlens_k, num_heads_kv: int, scale: float,
-                          causal: bool, tokens=None, key_range=None, row_block: int = 1024):
+                          causal: bool, tokens=None, key_range=None, row_block: int = 1024, causal_offset=None):
     """Attention for selected packed query tokens (all heads), TND layout.
 
     q [Tq, Hq, D], k / v [Tk, Hkv, D]; cu_seqlens_* int [B+1] ([P1] core
     optimisation 1). ``tokens`` is an iterable of packed query indices (None =
     all). ``key_range`` optionally restricts every sequence to keys
     [lo_b, hi_b) given as a callable b -> (lo, hi), with the mask still using
-    absolute positions. Returns O [len(tokens), Hq, D] and lse [len(tokens), Hq].
+    absolute positions. ``causal_offset`` (int [B] or None) replaces Lk - Lq
+    in the causal mask per sequence. Returns O [len(tokens), Hq, D] and
+    lse [len(tokens), Hq].
 
     [P1] core optimisation 5: query head h shares kv head h // (Hq / Hkv).
     """
@@ -149,7 +157,8 @@ def varlen_attention_rows(q, k, v, cu_seqlens_q, cu_seqlens_k, num_heads_kv: int
         for blk in range(0, len(sel), row_block):
             rows = sel[blk:blk + row_block]
             i_pos = tokens[rows] - qs                      # position inside the sequence
-            vis = _visible(i_pos, lq, lk, causal, lo, hi)
+            vis = _visible(i_pos, lq, lk, causal, lo, hi,
+                           None if causal_offset is None else causal_offset[b])
             for h in range(hq):
                 g = h // grp
                 o_h, lse_h = _attend_rows(q[tokens[rows], h, :], k[ks + lo:ks + hi, g, :],
@@ -160,7 +169,7 @@ def varlen_attention_rows(q, k, v, cu_seqlens_q, cu_seqlens_k, num_heads_kv: int
 
 
 def varlen_attention(q, k, v, cu_seqlens_q, cu_seqlens_k, num_heads_kv: int, scale: float,
-                     causal: bool, row_block: int = 1024):
+                     causal: bool, row_block: int = 1024, causal_offset=None):
     """Whole-batch varlen attention: O [Tq, Hq, D] and natural-log lse [Tq, Hq], fp64.
 
     The call [P1] 2.1 makes: TND layout, per-sequence lengths from cu_seqlens,
@@ -168,7 +177,7 @@ def varlen_attention(q, k, v, cu_seqlens_q, cu_seqlens_k, num_heads_kv: int, sca
     op for prefill (Lq = Lk) and decode (Lq = 1).
     """
     return varlen_attention_rows(q, k, v, cu_seqlens_q, cu_seqlens_k, num_heads_kv, scale,
-                                 causal, tokens=None, row_block=row_block)
+                                 causal, tokens=None, row_block=row_block, causal_offset=causal_offset)
 
 
 def attn_update(lse, go, update_type: int = 1):

@@ -67,8 +67,10 @@ def _rand_case(rng, batch, max_len, hq, hkv, d, allow_unequal=True, allow_empty=
     return lq, lk, q, k, v
 
 
-def brute_force(q, k, v, lengths_q, lengths_k, hq, hkv, scale, causal, d, dv):
-    """Pure-Python softmax attention from the definition, with math.fsum sums."""
+def brute_force(q, k, v, lengths_q, lengths_k, hq, hkv, scale, causal, d, dv, offsets=None):
+    """Pure-Python softmax attention from the definition, with math.fsum sums.
+
+    offsets[b] (optional): query i of sequence b sees key j iff j <= i + offsets[b]."""
     cu_q = [0]
     for x in lengths_q:
         cu_q.append(cu_q[-1] + int(x))
@@ -84,7 +86,8 @@ def brute_force(q, k, v, lengths_q, lengths_k, hq, hkv, scale, causal, d, dv):
             kvh = h // grp
             for i in range(lq):
                 t = cu_q[b] + i
-                keys = [j for j in range(lk) if (not causal) or j <= i + lk - lq]
+                lim = i + (lk - lq if offsets is None else offsets[b])
+                keys = [j for j in range(lk) if (not causal) or j <= lim]
                 if not keys:
                     continue
                 s = {j: scale * math.fsum(q[t][h][x] * k[cu_k[b] + j][kvh][x] for x in range(d))
@@ -395,6 +398,48 @@ def check_paged_scatter(orc, seed=17):
             assert np.all(np.isfinite(o_p))
 
 
+def check_causal_offset_brute_force(orc, n_cases=24, seed=19):
+    """Per-sequence causal offsets against the brute force, including offsets that hide every key
+    from some rows and offsets past the last key."""
+    rng = np.random.default_rng(seed)
+    for _ in range(n_cases):
+        batch = int(rng.integers(1, 4))
+        lq = rng.integers(0, 6, batch)
+        lk = rng.integers(0, 6, batch)
+        hq, hkv, d = 2, 1, 3
+        off = [int(rng.integers(-int(b) - 2, int(a) + int(b) + 3)) for a, b in zip(lq, lk)]
+        q = rng.standard_normal((int(lq.sum()), hq, d))
+        k = rng.standard_normal((int(lk.sum()), hkv, d))
+        v = rng.standard_normal((int(lk.sum()), hkv, d))
+        o, l = orc.varlen_attention(q, k, v, _cu(lq), _cu(lk), hkv, 0.7, True, causal_offset=off)
+        ob, lb = brute_force(q.tolist(), k.tolist(), v.tolist(), lq, lk, hq, hkv, 0.7, True, d, d, offsets=off)
+        _same(o, ob, 1e-12)
+        _same(l, lb, 1e-12)
+
+
+def check_causal_offset_chunks(orc, seed=23):
+    """A key chunk [a, c) of square causal sequences, packed alone and computed with offset -a, equals
+    the chunk partial that keeps absolute positions through key_range (chunked_partials)."""
+    rng = np.random.default_rng(seed)
+    lens = np.array([9, 1, 14, 6])
+    hq, hkv, d, sp = 4, 2, 5, 3
+    q = rng.standard_normal((int(lens.sum()), hq, d))
+    k = rng.standard_normal((int(lens.sum()), hkv, d))
+    v = rng.standard_normal((int(lens.sum()), hkv, d))
+    cu = _cu(lens)
+    lse_c, go_c = orc.chunked_partials(q, k, v, cu, cu, hkv, 0.5, True, sp)
+    for c in range(sp):
+        bounds = [((c * int(n)) // sp, ((c + 1) * int(n)) // sp) for n in lens]
+        kc = np.concatenate([k[cu[b] + lo:cu[b] + hi] for b, (lo, hi) in enumerate(bounds)])
+        vc = np.concatenate([v[cu[b] + lo:cu[b] + hi] for b, (lo, hi) in enumerate(bounds)])
+        o, l = orc.varlen_attention(q, kc, vc, cu, _cu([hi - lo for lo, hi in bounds]), hkv, 0.5, True,
+                                    causal_offset=[-lo for lo, _ in bounds])
+        assert np.allclose(o.reshape(-1, d), go_c[c], rtol=1e-13, atol=1e-13)
+        assert np.array_equal(np.isneginf(l.reshape(-1)), np.isneginf(lse_c[c]))
+        live = ~np.isneginf(lse_c[c])
+        assert np.allclose(l.reshape(-1)[live], lse_c[c][live], rtol=1e-13, atol=1e-13)
+
+
 ALL_CHECKS = [
     check_golden_attention,
     check_golden_merge,
@@ -407,4 +452,6 @@ ALL_CHECKS = [
     check_rows_subset,
     check_golden_paged,
     check_paged_scatter,
+    check_causal_offset_brute_force,
+    check_causal_offset_chunks,
 ]

@@ -15,8 +15,12 @@ SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), 
 
 MUTANTS = {
     "gqa_modulo_mapping": ("g = h // grp", "g = h % hkv"),
-    "causal_top_left": ("vis &= j <= (i_pos[:, None] + (lk - lq))", "vis &= j <= i_pos[:, None]"),
-    "causal_diagonal_masked": ("vis &= j <= (i_pos[:, None] + (lk - lq))", "vis &= j < (i_pos[:, None] + (lk - lq))"),
+    "causal_top_left": ("off = (lk - lq) if offset is None else int(offset)",
+                        "off = 0 if offset is None else int(offset)"),
+    "causal_diagonal_masked": ("vis &= j <= (i_pos[:, None] + off)", "vis &= j < (i_pos[:, None] + off)"),
+    "causal_offset_ignored": ("off = (lk - lq) if offset is None else int(offset)", "off = lk - lq"),
+    "causal_offset_sign": ("off = (lk - lq) if offset is None else int(offset)",
+                           "off = (lk - lq) if offset is None else -int(offset)"),
     "scale_dropped": ("s = scale * (q_rows @ k_seq.T)", "s = (q_rows @ k_seq.T)"),
     "lse_without_max": ("lse[has] = m[has] + np.log(l_sum[has])", "lse[has] = np.log(l_sum[has])"),
     "lse_log2": ("lse[has] = m[has] + np.log(l_sum[has])", "lse[has] = m[has] + np.log2(l_sum[has])"),
