@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define VFA_ABI_VERSION 2
+#define VFA_ABI_VERSION 3
 
 typedef enum vfa_status {
   VFA_OK = 0,
@@ -129,6 +129,39 @@ int32_t varlen_attn_fwd(const void* q, const void* k, const void* v, int32_t in_
                         float softmax_scale, int32_t causal,
                         void* out, int32_t out_dtype, float* lse,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* varlen_attn_fwd with an explicit causal alignment per sequence.
+ *
+ * Identical to varlen_attn_fwd except that, when causal != 0, query i of
+ * sequence b sees key j iff
+ *   j <= i + causal_offset[b]
+ * instead of j <= i + Lk_b - Lq_b. causal_offset[b] is the position of the
+ * sequence's first query minus the position of its first key, so:
+ *   - Lk_b - Lq_b reproduces varlen_attn_fwd (queries are the last Lq_b
+ *     positions of the key sequence);
+ *   - 0 aligns the first query with the first key (top-left);
+ *   - -a computes the partial of a key chunk [a, c) of a sequence against
+ *     all of its queries with the sequence's absolute causal mask: the
+ *     per-chunk partials of [P4]'s sequence-parallel setting, which
+ *     attn_update then merges. With the query shard starting at position s,
+ *     the offset is s - a.
+ * Rows that see no key get out = 0 and lse = -inf. Any int32 value is
+ * accepted (values beyond -Lq_b or Lk_b act as those bounds).
+ *
+ * causal_offset: device int32 [batch]; required (non-NULL) when causal != 0,
+ *         ignored when causal == 0. Every other argument, the supported set
+ *         and the workspace are those of varlen_attn_fwd (same
+ *         varlen_attn_fwd_workspace_size).
+ */
+int32_t varlen_attn_fwd_offset(const void* q, const void* k, const void* v, int32_t in_dtype,
+                               const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                               const int32_t* causal_offset,
+                               int32_t batch, int32_t total_q, int32_t total_k,
+                               int32_t max_seqlen_q, int32_t max_seqlen_k,
+                               int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                               float softmax_scale, int32_t causal,
+                               void* out, int32_t out_dtype, float* lse,
+                               void* workspace, size_t workspace_bytes, void* stream);
 
 /* AttentionUpdate merge ([P4], operator function description):
  *   lse_max = max_i lse[i, r]

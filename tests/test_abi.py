@@ -44,7 +44,7 @@ def test_exports_match_header(lib):
 
 
 def test_abi_version(lib):
-    assert lib.vfa_abi_version() == vfa._header_abi_version() == 2
+    assert lib.vfa_abi_version() == vfa._header_abi_version() == 3
 
 
 def test_status_strings(lib):
@@ -104,6 +104,17 @@ def _fwd(lib, **kw):
 ])
 def test_fwd_validation(lib, kw, code):
     assert _fwd(lib, **kw) == code
+
+
+def test_fwd_offset_validation(lib):
+    a = (P, P, P, BF16, P, P)
+    rest = (2, 8, 8, 4, 4, 4, 2, 128, 0.125)
+    tail = (P, BF16, P, None, 0, None)
+    off = lib.varlen_attn_fwd_offset
+    assert off(*a, None, *rest, 1, *tail) == NULL                     # causal needs the offsets
+    assert off(*a, None, 0, 8, 8, 4, 4, 4, 2, 128, 0.125, 1, *tail) == OK   # empty batch
+    assert off(*a, P, 2, 8, 8, 4, 4, 4, 2, 96, 0.125, 1, *tail) == UNSUP     # same checks as varlen_attn_fwd
+    assert off(*a, P, -1, 8, 8, 4, 4, 4, 2, 128, 0.125, 1, *tail) == SHAPE
 
 
 def _upd(lib, **kw):

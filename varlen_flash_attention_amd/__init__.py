@@ -10,7 +10,8 @@ the library has not been built the first call raises.
 
 Entry points (same names as the C ABI in include/vfa.h):
   varlen_attn_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
-                  softmax_scale=None, causal=True, out_dtype=None) -> (out, lse)
+                  softmax_scale=None, causal=True, out_dtype=None, causal_offset=None) -> (out, lse)
+      (with causal_offset given: the C entry point varlen_attn_fwd_offset)
   attn_update(lse, go, update_type=1) -> (out, lse_out or None)
   varlen_last_token_gather(x, cu_seqlens) -> x[cu_seqlens[1:] - 1]
   varlen_attn_fwd_workspace_size(...) -> bytes
@@ -91,6 +92,16 @@ def load_library() -> ctypes.CDLL:
         c.c_void_p, c.c_int32, c.c_void_p,                      # out out_dtype lse
         c.c_void_p, c.c_size_t, c.c_void_p,                     # workspace bytes stream
     ]
+    lib.varlen_attn_fwd_offset.restype = c.c_int32
+    lib.varlen_attn_fwd_offset.argtypes = [
+        c.c_void_p, c.c_void_p, c.c_void_p, c.c_int32,          # q k v in_dtype
+        c.c_void_p, c.c_void_p, c.c_void_p,                     # cu_q cu_k causal_offset
+        c.c_int32, c.c_int32, c.c_int32, c.c_int32, c.c_int32,  # batch total_q total_k max_q max_k
+        c.c_int32, c.c_int32, c.c_int32,                        # hq hkv d
+        c.c_float, c.c_int32,                                   # scale causal
+        c.c_void_p, c.c_int32, c.c_void_p,                      # out out_dtype lse
+        c.c_void_p, c.c_size_t, c.c_void_p,                     # workspace bytes stream
+    ]
     lib.attn_update.restype = c.c_int32
     lib.attn_update.argtypes = [c.c_void_p, c.c_void_p, c.c_int32, c.c_int32, c.c_int64, c.c_int32,
                                 c.c_int32, c.c_void_p, c.c_void_p, c.c_void_p]
@@ -165,12 +176,14 @@ def varlen_attn_fwd_workspace_size(batch, total_q, max_seqlen_q, max_seqlen_k, n
 
 def varlen_attn_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
                     softmax_scale: float | None = None, causal: bool = True, out_dtype=None,
-                    out=None, lse=None, workspace=None):
+                    out=None, lse=None, workspace=None, causal_offset=None):
     """Attention over packed sequences (TND). Returns (out [Tq,Hq,D], lse [Tq,Hq] fp32).
 
     q [Tq, Hq, D], k / v [Tk, Hkv, D] (bf16 or fp32, same dtype); cu_seqlens_*
     int32 [B+1] on the GPU. max_seqlen_* are host upper bounds of the lengths.
-    Default scale 1/sqrt(D); default out dtype = input dtype.
+    Default scale 1/sqrt(D); default out dtype = input dtype. causal_offset
+    (int32 [B] on the GPU): query i of sequence b sees key j iff
+    j <= i + causal_offset[b] (default Lk - Lq, bottom-right).
     """
     torch = _torch()
     lib = load_library()
@@ -205,13 +218,25 @@ def varlen_attn_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_
     if ws_bytes and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     ws_ptr = workspace.data_ptr() if (ws_bytes and workspace is not None) else None
-    st = lib.varlen_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), in_code,
-                             cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(),
-                             batch, tq, tk, int(max_seqlen_q), int(max_seqlen_k), hq, hkv, d,
-                             scale, 1 if causal else 0, out.data_ptr(), out_code, lse.data_ptr(),
-                             ws_ptr, ws_bytes, _stream_ptr(q.device))
+    if causal_offset is None:
+        st = lib.varlen_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), in_code,
+                                 cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(),
+                                 batch, tq, tk, int(max_seqlen_q), int(max_seqlen_k), hq, hkv, d,
+                                 scale, 1 if causal else 0, out.data_ptr(), out_code, lse.data_ptr(),
+                                 ws_ptr, ws_bytes, _stream_ptr(q.device))
+        if st != 0:
+            raise VfaError(st, "varlen_attn_fwd")
+        return out, lse
+    _check_gpu("causal_offset", causal_offset, 1)
+    if causal_offset.dtype != torch.int32 or int(causal_offset.shape[0]) != batch:
+        raise ValueError("causal_offset must be int32 with one entry per sequence")
+    st = lib.varlen_attn_fwd_offset(q.data_ptr(), k.data_ptr(), v.data_ptr(), in_code,
+                                    cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), causal_offset.data_ptr(),
+                                    batch, tq, tk, int(max_seqlen_q), int(max_seqlen_k), hq, hkv, d,
+                                    scale, 1 if causal else 0, out.data_ptr(), out_code, lse.data_ptr(),
+                                    ws_ptr, ws_bytes, _stream_ptr(q.device))
     if st != 0:
-        raise VfaError(st, "varlen_attn_fwd")
+        raise VfaError(st, "varlen_attn_fwd_offset")
     return out, lse
 
 

@@ -102,12 +102,13 @@ VFA_API size_t varlen_attn_fwd_workspace_size(int32_t batch, int32_t total_q, in
   return p.use ? p.ws_bytes : 0;
 }
 
-VFA_API int32_t varlen_attn_fwd(const void* q, const void* k, const void* v, int32_t in_dtype,
-                                const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t batch,
-                                int32_t total_q, int32_t total_k, int32_t max_seqlen_q, int32_t max_seqlen_k,
-                                int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
-                                float softmax_scale, int32_t causal, void* out, int32_t out_dtype, float* lse,
-                                void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+
+int32_t attn_fwd_impl(const void* q, const void* k, const void* v, int32_t in_dtype, const int32_t* cu_seqlens_q,
+                      const int32_t* cu_seqlens_k, const int32_t* causal_offset, int32_t batch, int32_t total_q,
+                      int32_t total_k, int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t num_heads_q,
+                      int32_t num_heads_kv, int32_t head_dim, float softmax_scale, int32_t causal, void* out,
+                      int32_t out_dtype, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   if (batch < 0 || total_q < 0 || total_k < 0 || max_seqlen_q < 0 || max_seqlen_k < 0) return VFA_ERR_SHAPE;
   if (batch == 0 || total_q == 0) return VFA_OK;
   if (!q || !k || !v || !cu_seqlens_q || !cu_seqlens_k || !out || !lse) return VFA_ERR_NULL;
@@ -137,7 +138,7 @@ VFA_API int32_t varlen_attn_fwd(const void* q, const void* k, const void* v, int
 
   vfa::AttnArgs a{};
   a.q = q; a.k = k; a.v = v;
-  a.cu_q = cu_seqlens_q; a.cu_k = cu_seqlens_k;
+  a.cu_q = cu_seqlens_q; a.cu_k = cu_seqlens_k; a.causal_off = causal_offset;
   a.batch = batch; a.total_q = total_q; a.total_k = total_k;
   a.max_seqlen_q = max_seqlen_q; a.max_seqlen_k = max_seqlen_k;
   a.hq = num_heads_q; a.hkv = num_heads_kv; a.grp = num_heads_q / num_heads_kv; a.head_dim = head_dim;
@@ -154,6 +155,32 @@ VFA_API int32_t varlen_attn_fwd(const void* q, const void* k, const void* v, int
     return vfa::launch_attn_decode_bf16(a, plan) == 0 ? VFA_OK : VFA_ERR_LAUNCH;
   }
   return vfa::launch_attn_fwd_bf16(a) == 0 ? VFA_OK : VFA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+VFA_API int32_t varlen_attn_fwd(const void* q, const void* k, const void* v, int32_t in_dtype,
+                                const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t batch,
+                                int32_t total_q, int32_t total_k, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                                float softmax_scale, int32_t causal, void* out, int32_t out_dtype, float* lse,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  return attn_fwd_impl(q, k, v, in_dtype, cu_seqlens_q, cu_seqlens_k, nullptr, batch, total_q, total_k,
+                       max_seqlen_q, max_seqlen_k, num_heads_q, num_heads_kv, head_dim, softmax_scale, causal, out,
+                       out_dtype, lse, workspace, workspace_bytes, stream);
+}
+
+VFA_API int32_t varlen_attn_fwd_offset(const void* q, const void* k, const void* v, int32_t in_dtype,
+                                       const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                       const int32_t* causal_offset, int32_t batch, int32_t total_q,
+                                       int32_t total_k, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                       int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                                       float softmax_scale, int32_t causal, void* out, int32_t out_dtype,
+                                       float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  if (batch > 0 && total_q > 0 && causal != 0 && !causal_offset) return VFA_ERR_NULL;
+  return attn_fwd_impl(q, k, v, in_dtype, cu_seqlens_q, cu_seqlens_k, causal != 0 ? causal_offset : nullptr,
+                       batch, total_q, total_k, max_seqlen_q, max_seqlen_k, num_heads_q, num_heads_kv, head_dim,
+                       softmax_scale, causal, out, out_dtype, lse, workspace, workspace_bytes, stream);
 }
 
 VFA_API int32_t attn_update(const float* lse, const void* go, int32_t go_dtype, int32_t sp, int64_t bsh,

@@ -61,6 +61,7 @@ struct SplitArgs {
   const bf16* v;
   const int32_t* cu_q;          // [batch + 1]
   const int32_t* cu_k;          // contiguous: [batch + 1]
+  const int32_t* causal_off;    // contiguous: per-sequence causal offset, or NULL (bottom-right)
   const int32_t* seqused_k;     // paged: keys of each sequence [batch]
   const int32_t* block_table;   // paged: [batch, max_pages]
   int batch, hq, hkv, grp, chunk, n_splits;
@@ -155,7 +156,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decode_split_kernel(const Sp
     if (lq <= 0 || key_lo >= lk) return;                 // this split holds no key of the sequence
   }
   const int key_hi = min(lk, key_lo + p.chunk);
-  const int diag = lk - lq;
+  const int diag = causal_diag(PAGED ? nullptr : p.causal_off, b, lq, lk);
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -498,7 +499,7 @@ int launch_t(const AttnArgs& a, const DecodePlan& p) {
   if (blocks > 0x7fffffffLL) return -1;
   SplitArgs s{};
   s.q = (const bf16*)a.q; s.k = (const bf16*)a.k; s.v = (const bf16*)a.v;
-  s.cu_q = a.cu_q; s.cu_k = a.cu_k;
+  s.cu_q = a.cu_q; s.cu_k = a.cu_k; s.causal_off = a.causal_off;
   s.batch = a.batch; s.hq = a.hq; s.hkv = a.hkv; s.grp = a.grp; s.chunk = p.chunk; s.n_splits = p.n_splits;
   s.n_cg = 1; s.rows_total = rows;
   s.scale = a.scale; s.scale_log2 = a.scale * kLog2e;

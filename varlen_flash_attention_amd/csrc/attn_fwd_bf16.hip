@@ -90,9 +90,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, Shape<WAVES, NQ>::THREA
                           amdgpu_waves_per_eu(Shape<WAVES, NQ>::WAVES_PER_EU, Shape<WAVES, NQ>::WAVES_PER_EU))) void
 attn_fwd_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int batch, int hq, int hkv,
-    int grp, int tokw, int n_mtiles, float scale, float scale_log2, OutT* __restrict__ out,
-    float* __restrict__ lse) {
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, const int32_t* __restrict__ coff,
+    int batch, int hq, int hkv, int grp, int tokw, int n_mtiles, float scale, float scale_log2,
+    OutT* __restrict__ out, float* __restrict__ lse) {
   constexpr int kThreads = Shape<WAVES, NQ>::THREADS;
   using S = Smem<D, kThreads>;
   __shared__ __attribute__((aligned(16))) char smem[S::TOTAL];
@@ -122,7 +122,7 @@ attn_fwd_bf16_kernel(
   const int k0 = cu_k[b];
   const int lk = cu_k[b + 1] - k0;
   const int tok_hi = min(lq, tok_lo + tokw);
-  const int diag = lk - lq;  // query i sees key j iff j <= i + diag (causal)
+  const int diag = causal_diag(coff, b, lq, lk);  // query i sees key j iff j <= i + diag (causal)
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -430,8 +430,8 @@ int launch_t(const AttnArgs& a) {
   if (blocks > 0x7fffffffLL) return -1;
   hipLaunchKernelGGL((attn_fwd_bf16_kernel<WAVES, NQ, D, CAUSAL, OutT>), dim3((unsigned)blocks),
                      dim3(Shape<WAVES, NQ>::THREADS), 0, (hipStream_t)a.stream, (const bf16*)a.q,
-                     (const bf16*)a.k, (const bf16*)a.v, a.cu_q, a.cu_k, a.batch, a.hq, a.hkv, a.grp, tokw,
-                     n_mtiles, a.scale, a.scale * kLog2e, (OutT*)a.out, a.lse);
+                     (const bf16*)a.k, (const bf16*)a.v, a.cu_q, a.cu_k, a.causal_off, a.batch, a.hq, a.hkv,
+                     a.grp, tokw, n_mtiles, a.scale, a.scale * kLog2e, (OutT*)a.out, a.lse);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -18,8 +18,8 @@ namespace {
 template <int D>
 __global__ __launch_bounds__(64) void attn_fwd_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
-    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int batch, int hq, int hkv,
-    int grp, long long rows_total, float scale, int causal, float* __restrict__ out,
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, const int32_t* __restrict__ coff,
+    int batch, int hq, int hkv, int grp, long long rows_total, float scale, int causal, float* __restrict__ out,
     float* __restrict__ lse) {
   const long long row = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (row >= rows_total) return;
@@ -36,7 +36,7 @@ __global__ __launch_bounds__(64) void attn_fwd_f32_kernel(
   const int k0 = cu_k[lo];
   const int lk = cu_k[lo + 1] - k0;
   int n_end = lk;
-  if (causal) n_end = max(0, min(lk, i + (lk - lq) + 1));
+  if (causal) n_end = max(0, min(lk, i + causal_diag(coff, lo, lq, lk) + 1));
 
   float qr[D], o[D];
   const float* qp = q + row * D;
@@ -75,8 +75,8 @@ int launch_t(const AttnArgs& a) {
   const long long blocks = (rows + 63) / 64;
   if (blocks > 0x7fffffffLL) return -1;
   hipLaunchKernelGGL((attn_fwd_f32_kernel<D>), dim3((unsigned)blocks), dim3(64), 0, (hipStream_t)a.stream,
-                     (const float*)a.q, (const float*)a.k, (const float*)a.v, a.cu_q, a.cu_k, a.batch, a.hq,
-                     a.hkv, a.grp, rows, a.scale, a.causal, (float*)a.out, a.lse);
+                     (const float*)a.q, (const float*)a.k, (const float*)a.v, a.cu_q, a.cu_k, a.causal_off,
+                     a.batch, a.hq, a.hkv, a.grp, rows, a.scale, a.causal, (float*)a.out, a.lse);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -54,6 +54,17 @@ __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
 template <typename T>
 __device__ __forceinline__ float to_f32(T x) { return (float)x; }
 
+// Causal diagonal of sequence b: query i sees key j iff j <= i + diag. The
+// caller's offset (the position of the sequence's first query minus that of
+// its first key), or Lk - Lq when there is none (bottom-right alignment), is
+// clamped to [-lq, lk]: that keeps every visible set (no offset can show more
+// than all keys or hide more than every row) and keeps i + diag from
+// overflowing.
+__device__ __forceinline__ int causal_diag(const int32_t* off, int b, int lq, int lk) {
+  const int d = off ? off[b] : lk - lq;
+  return d < -lq ? -lq : (d > lk ? lk : d);
+}
+
 // ---------------------------------------------------------------------------
 // AttentionUpdate merge statistics for one row over n partials ("attention_update
 // operator optimisation practice", operator function description):

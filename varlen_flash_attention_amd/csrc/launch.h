@@ -13,6 +13,7 @@ struct AttnArgs {
   const void* v;
   const int32_t* cu_q;
   const int32_t* cu_k;
+  const int32_t* causal_off;  // per-sequence causal offset, or NULL for Lk - Lq (bottom-right)
   int batch, total_q, total_k, max_seqlen_q, max_seqlen_k;
   int hq, hkv, grp, head_dim;
   float scale;
