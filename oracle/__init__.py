@@ -21,6 +21,10 @@ Parity status per function (what pins it; see tests/test_oracle_*.py):
       (Q = 0, so each row is the mean of the value rows it gathers) and
       scatter-into-shuffled-pages equals the contiguous oracle, with NaN in
       every slot the block table does not name.
+  prologue.rms_norm / rotary / qk_norm_rope -- pinned: a hand-worked value
+      (tests/golden/qk_norm_rope_handworked.json), torch's fp64 rms_norm,
+      the rotation as complex multiplication by exp(i theta), identity at
+      position 0, and the pair norms it preserves.
 """
 from .attention import (  # noqa: F401
     varlen_attention,
@@ -30,4 +34,10 @@ from .attention import (  # noqa: F401
     chunked_partials,
     paged_gather,
     paged_attention_rows,
+)
+from .prologue import (  # noqa: F401
+    rms_norm,
+    rotate_half,
+    rotary,
+    qk_norm_rope,
 )

@@ -455,3 +455,78 @@ ALL_CHECKS = [
     check_causal_offset_brute_force,
     check_causal_offset_chunks,
 ]
+
+
+# ------------------------------------------------------------------ attention prologue (oracle/prologue.py)
+
+def check_golden_qk_norm_rope(pro):
+    g = _load("qk_norm_rope_handworked.json")
+    x = np.array(g["x"], dtype=np.float64).reshape(1, 1, -1)
+    cos = np.array(g["cos"], dtype=np.float64).reshape(1, -1)
+    sin = np.array(g["sin"], dtype=np.float64).reshape(1, -1)
+    q_out, k_out = pro.qk_norm_rope(x, x, g["weight"], g["k_weight"], cos, sin, g["eps"])
+    want = np.array(g["out_times_sqrt_7_5"], dtype=np.float64) / math.sqrt(7.5)
+    want_k = np.array(g["k_out_times_sqrt_7_5"], dtype=np.float64) / math.sqrt(7.5)
+    assert np.allclose(q_out.reshape(-1), want, rtol=1e-15, atol=1e-15), (q_out, want)
+    assert np.allclose(k_out.reshape(-1), want_k, rtol=1e-15, atol=1e-15), (k_out, want_k)
+
+
+def check_rms_norm_torch(pro, seed=29):
+    """torch's fp64 CPU rms_norm over the last dimension (a library routine) with a weight and eps."""
+    import torch
+    rng = np.random.default_rng(seed)
+    for d, eps in ((128, 1e-6), (64, 0.1), (8, 2.0)):
+        x = rng.standard_normal((5, 3, d)) * 3.0
+        w = 1.0 + 0.2 * rng.standard_normal(d)
+        ref = torch.nn.functional.rms_norm(torch.from_numpy(x), (d,), torch.from_numpy(w), eps).numpy()
+        assert np.allclose(pro.rms_norm(x, w, eps), ref, rtol=1e-13, atol=1e-13)
+
+
+def _angle_tables(rng, t, d):
+    theta = rng.uniform(-math.pi, math.pi, (t, d // 2))
+    emb = np.concatenate([theta, theta], axis=-1)
+    return theta, np.cos(emb), np.sin(emb)
+
+
+def check_rotary_complex(pro, seed=31):
+    """With cos / sin built from angles (the same angle for d and d + D/2), the rotation is the complex
+    product (y[:D/2] + i y[D/2:]) * exp(i theta): an independent way to write it."""
+    rng = np.random.default_rng(seed)
+    t, n, d = 6, 3, 16
+    y = rng.standard_normal((t, n, d))
+    theta, cos, sin = _angle_tables(rng, t, d)
+    z = (y[..., :d // 2] + 1j * y[..., d // 2:]) * np.exp(1j * theta)[:, None, :]
+    want = np.concatenate([z.real, z.imag], axis=-1)
+    assert np.allclose(pro.rotary(y, cos, sin), want, rtol=1e-13, atol=1e-13)
+
+
+def check_rotary_identity_and_pair_norms(pro, seed=37):
+    rng = np.random.default_rng(seed)
+    t, n, d = 4, 2, 8
+    y = rng.standard_normal((t, n, d))
+    assert np.array_equal(pro.rotary(y, np.ones((t, d)), np.zeros((t, d))), y)        # position 0
+    _, cos, sin = _angle_tables(rng, t, d)
+    out = pro.rotary(y, cos, sin)
+    h = d // 2
+    assert np.allclose(out[..., :h] ** 2 + out[..., h:] ** 2, y[..., :h] ** 2 + y[..., h:] ** 2, rtol=1e-13)
+
+
+def check_rms_norm_invariants(pro, seed=41):
+    """eps = 0: the output is unchanged by a positive scale, negated by a negative one, and its
+    mean square is 1 with a unit weight."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((7, 2, 32))
+    one = np.ones(32)
+    base = pro.rms_norm(x, one, 0.0)
+    assert np.allclose(pro.rms_norm(5.0 * x, one, 0.0), base, rtol=1e-14, atol=1e-14)
+    assert np.allclose(pro.rms_norm(-0.25 * x, one, 0.0), -base, rtol=1e-14, atol=1e-14)
+    assert np.allclose(np.mean(base ** 2, axis=-1), 1.0, rtol=1e-14)
+
+
+PROLOGUE_CHECKS = [
+    check_golden_qk_norm_rope,
+    check_rms_norm_torch,
+    check_rotary_complex,
+    check_rotary_identity_and_pair_norms,
+    check_rms_norm_invariants,
+]

@@ -11,7 +11,9 @@ import pytest
 
 from tests import oracle_pins as pins
 
-SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "attention.py")
+ORACLE_DIR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle")
+SRC = os.path.join(ORACLE_DIR, "attention.py")
+PROLOGUE_SRC = os.path.join(ORACLE_DIR, "prologue.py")
 
 MUTANTS = {
     "gqa_modulo_mapping": ("g = h // grp", "g = h % hkv"),
@@ -43,12 +45,25 @@ MUTANTS = {
 }
 
 
-def _mutant_module(old, new):
-    with open(SRC) as fh:
+PROLOGUE_MUTANTS = {
+    "rotate_half_sign": ("np.concatenate([-x[..., h:], x[..., :h]], axis=-1)",
+                         "np.concatenate([x[..., h:], -x[..., :h]], axis=-1)"),
+    "rotate_half_no_swap": ("np.concatenate([-x[..., h:], x[..., :h]], axis=-1)",
+                            "np.concatenate([-x[..., :h], x[..., h:]], axis=-1)"),
+    "cos_sin_swapped": ("return x * c + rotate_half(x) * s", "return x * s + rotate_half(x) * c"),
+    "rms_sum_not_mean": ("np.mean(x * x, axis=-1, keepdims=True)", "np.sum(x * x, axis=-1, keepdims=True)"),
+    "rms_eps_outside_sqrt": ("x / np.sqrt(var + eps)", "x / (np.sqrt(var) + eps)"),
+    "rms_weight_dropped": ("* np.asarray(weight, dtype=np.float64)", "* 1.0"),
+    "k_takes_q_weight": ("rotary(rms_norm(k, k_weight, eps), cos, sin)", "rotary(rms_norm(k, q_weight, eps), cos, sin)"),
+}
+
+
+def _mutant_module(old, new, path=SRC):
+    with open(path) as fh:
         src = fh.read()
     assert src.count(old) == 1, f"mutation site not found exactly once: {old!r}"
     mod = types.ModuleType("oracle_mutant")
-    exec(compile(src.replace(old, new), SRC + " (mutant)", "exec"), mod.__dict__)
+    exec(compile(src.replace(old, new), path + " (mutant)", "exec"), mod.__dict__)
     return mod
 
 
@@ -67,4 +82,22 @@ def test_mutant_is_caught(name):
 def test_unmutated_copy_passes():
     mod = _mutant_module("import numpy as np", "import numpy as np")
     for check in pins.ALL_CHECKS:
+        check(mod)
+
+
+@pytest.mark.parametrize("name", sorted(PROLOGUE_MUTANTS))
+def test_prologue_mutant_is_caught(name):
+    mod = _mutant_module(*PROLOGUE_MUTANTS[name], path=PROLOGUE_SRC)
+    caught = []
+    for check in pins.PROLOGUE_CHECKS:
+        try:
+            check(mod)
+        except Exception as exc:  # noqa: BLE001 - any failure counts as caught
+            caught.append((check.__name__, type(exc).__name__))
+    assert caught, f"no pin catches prologue mutant {name}"
+
+
+def test_unmutated_prologue_passes():
+    mod = _mutant_module("import numpy as np", "import numpy as np", path=PROLOGUE_SRC)
+    for check in pins.PROLOGUE_CHECKS:
         check(mod)

@@ -8,3 +8,8 @@ from tests import oracle_pins as pins
 @pytest.mark.parametrize("check", pins.ALL_CHECKS, ids=lambda f: f.__name__)
 def test_oracle_pin(check):
     check(oracle)
+
+
+@pytest.mark.parametrize("check", pins.PROLOGUE_CHECKS, ids=lambda f: f.__name__)
+def test_prologue_pin(check):
+    check(oracle.prologue)
