@@ -11,8 +11,9 @@ head, key), masked pairs excluded. One JSON line is printed.
 
 Extra fields (not the headline): the embedding-style prefill with the
 last-token gather, the same long prefill without masking, decode against
-long KV sets (contiguous, and paged with 16- and 128-key pages), and the
-attn_update merge of the chunked-context config (sp=8, bsh=2048, hd=128,
+long KV sets (contiguous, and paged with 16- and 128-key pages), the q/k
+RMSNorm + rotary prologue on the long-prefill tokens, and the attn_update
+merge of the chunked-context config (sp=8, bsh=2048, hd=128,
 fp32) timed with caches flushed before every rep.
 
 "roofline" is the attention kernel's achieved useful FLOP rate (per-launch
@@ -153,6 +154,38 @@ def paged_case(vfa, torch, w, page_size, reps=20, warmup=3):
     res = attn_stats(w, ms, extra_bytes=int(sum(-(-int(n) // page_size) for n in w.lengths_k)) * 4)
     res["page_size"] = page_size
     del q, kc, vc, table, used, cu_q, out, lse, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def prologue_case(vfa, torch, lengths, reps=20, warmup=3):
+    """qk_norm_rope on the long-prefill tokens (Hq=32, Hkv=8, D=128): q and k read and written once,
+    one fp32 cos / sin row per token."""
+    import numpy as np
+    from varlen_flash_attention_amd.workloads import bf16_bits, make_prologue
+
+    p = make_prologue(lengths, 32, 8, 128, seed=9)
+
+    def dev(x):
+        return torch.from_numpy(bf16_bits(x).view(np.int16)).cuda().view(torch.bfloat16)
+
+    q, k, wq, wk = dev(p.q), dev(p.k), dev(p.q_weight), dev(p.k_weight)
+    cos, sin = torch.from_numpy(p.cos).cuda(), torch.from_numpy(p.sin).cuda()
+    qo, ko = torch.empty_like(q), torch.empty_like(k)
+
+    def call():
+        vfa.qk_norm_rope(q, k, wq, wk, cos, sin, eps=p.eps, q_out=qo, k_out=ko)
+
+    ms = time_calls(call, reps, warmup, torch)
+    t = median(ms)
+    tokens = int(p.lengths.sum())
+    qk_bytes = tokens * (32 + 8) * 128 * 2
+    byt = 2 * qk_bytes + 2 * tokens * 128 * 4 + 2 * 128 * 2
+    res = {"ms_median": round(t, 4), "ms_p10": round(sorted(ms)[len(ms) // 10], 4),
+           "ms_p90": round(sorted(ms)[(9 * len(ms)) // 10], 4), "compulsory_mb": round(byt / 1e6, 2),
+           "gb_per_s": round(byt / t / 1e6, 1), "frac_hbm_peak": round(byt / t / 1e6 / PEAK_HBM_GBPS, 4),
+           "tokens": tokens}
+    del q, k, wq, wk, cos, sin, qo, ko
     torch.cuda.empty_cache()
     return res
 
@@ -346,6 +379,8 @@ def main() -> int:
             log(f"[bench] extra: paged decode, {page}-key pages")
             extra[f"paged_decode_p{page}"] = paged_case(vfa, torch, wd, page)
         del wd
+        log("[bench] extra: q/k RMSNorm + rotary prologue")
+        extra["qk_norm_rope"] = prologue_case(vfa, torch, w.lengths_q)
         log("[bench] extra: attn_update merge")
         extra["attn_update_merge"] = merge_case(vfa, torch)
 

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define VFA_ABI_VERSION 3
+#define VFA_ABI_VERSION 4
 
 typedef enum vfa_status {
   VFA_OK = 0,
@@ -242,6 +242,39 @@ int32_t paged_attn_decode(const void* q, int32_t in_dtype,
                           float softmax_scale, int32_t causal,
                           void* out, int32_t out_dtype, float* lse,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Attention prologue on TND tensors: per-head RMSNorm of q and k, then the
+ * rotary embedding ([P1] 2.2 normalisation layer, 2.3 q_norm / k_norm on the
+ * [T, heads, head_dim] view, 2.4 rotary embedding with per-token cos / sin).
+ *
+ * For every token t and head h of q (weight q_weight) and of k (k_weight):
+ *   r   = x / sqrt(mean_d x[d]^2 + eps)            x = in[t, h, :]
+ *   y   = r * weight
+ *   out[t, h, d] = y[d] * cos[t, d] + rot[d] * sin[t, d],
+ *   rot = [-y[D/2:], y[:D/2]]                      (rotate-half form)
+ * computed in fp32 and rounded once to bf16. The page gives npu_rotary_mul
+ * without its formula; the rotate-half form is the reading taken.
+ *
+ * q_in / q_out  [total_tokens, num_heads_q, head_dim]   bf16
+ * k_in / k_out  [total_tokens, num_heads_kv, head_dim]  bf16
+ *               (out may be the same buffer as in: each row is read before
+ *               it is written; the two must not overlap otherwise)
+ * q_weight, k_weight  [head_dim] bf16
+ * cos, sin      [total_tokens, head_dim] fp32, one row per token for all of
+ *               its heads (positions are the caller's: in TND each sequence
+ *               usually restarts at 0)
+ * dtype         VFA_BF16 (the only supported value)
+ * eps           finite, >= 0
+ * Supported: head_dim 64 or 128. Pointers 16-byte aligned. num_heads_q or
+ * num_heads_kv may be 0 (that side's pointers may then be NULL).
+ * total_tokens == 0 returns VFA_OK.
+ */
+int32_t qk_norm_rope(const void* q_in, const void* k_in, int32_t dtype,
+                     const void* q_weight, const void* k_weight,
+                     const float* cos, const float* sin,
+                     int32_t total_tokens, int32_t num_heads_q, int32_t num_heads_kv,
+                     int32_t head_dim, float eps,
+                     void* q_out, void* k_out, void* stream);
 
 /* Last-token gather ([P1] core optimisation 1, embed(): x[cu_seqlens[1:] - 1]).
  *

@@ -44,7 +44,7 @@ def test_exports_match_header(lib):
 
 
 def test_abi_version(lib):
-    assert lib.vfa_abi_version() == vfa._header_abi_version() == 3
+    assert lib.vfa_abi_version() == vfa._header_abi_version() == 4
 
 
 def test_status_strings(lib):
@@ -233,3 +233,34 @@ def test_paged_workspace_plan(lib):
     assert ws(2, 2, 1, 40000, 32, 1, 64) == 157 * 2 * 32 * 65 * 4              # 2 units: 256-key splits
     assert ws(64, 64, 1, 256, 32, 4, 128) == 0                                  # one split
     assert ws(0, 0, 1, 4096, 32, 4, 128) == 0
+
+
+def _qknr(lib, **kw):
+    a = dict(q=P, k=P, dtype=BF16, wq=P, wk=P, cos=P, sin=P, t=16, hq=32, hkv=8, d=128, eps=1e-6, qo=P, ko=P,
+             stream=None)
+    a.update(kw)
+    return lib.qk_norm_rope(a["q"], a["k"], a["dtype"], a["wq"], a["wk"], a["cos"], a["sin"], a["t"], a["hq"],
+                            a["hkv"], a["d"], a["eps"], a["qo"], a["ko"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(t=0), OK),
+    (dict(hq=0, hkv=0), OK),
+    (dict(t=0, q=None), OK),
+    (dict(t=-1), SHAPE),
+    (dict(hq=-1), SHAPE),
+    (dict(cos=None), NULL),
+    (dict(sin=None), NULL),
+    (dict(q=None), NULL),
+    (dict(wk=None), NULL),
+    (dict(ko=None), NULL),
+    (dict(d=96), UNSUP),
+    (dict(dtype=F32), UNSUP),
+    (dict(eps=-1.0), UNSUP),
+    (dict(eps=float("nan")), UNSUP),
+    (dict(q=P + 2), UNSUP),
+    (dict(cos=P + 4), UNSUP),
+    (dict(hkv=0, k=None, wk=None, ko=None, d=96), UNSUP),   # k side unused: only the head_dim check fails
+])
+def test_qk_norm_rope_validation(lib, kw, code):
+    assert _qknr(lib, **kw) == code

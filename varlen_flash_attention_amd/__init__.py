@@ -18,6 +18,7 @@ Entry points (same names as the C ABI in include/vfa.h):
   paged_attn_decode(q, k_cache, v_cache, block_table, cu_seqlens_q, seqused_k, max_seqlen_q,
                     max_seqlen_k, softmax_scale=None, causal=True, out_dtype=None) -> (out, lse)
   paged_attn_decode_workspace_size(...) -> bytes
+  qk_norm_rope(q, k, q_weight, k_weight, cos, sin, eps=1e-6, q_out=None, k_out=None) -> (q_out, k_out)
 """
 from __future__ import annotations
 
@@ -38,6 +39,7 @@ __all__ = [
     "varlen_last_token_gather",
     "paged_attn_decode",
     "paged_attn_decode_workspace_size",
+    "qk_norm_rope",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -121,6 +123,10 @@ def load_library() -> ctypes.CDLL:
         c.c_void_p, c.c_int32, c.c_void_p,                      # out out_dtype lse
         c.c_void_p, c.c_size_t, c.c_void_p,                     # workspace bytes stream
     ]
+    lib.qk_norm_rope.restype = c.c_int32
+    lib.qk_norm_rope.argtypes = [c.c_void_p, c.c_void_p, c.c_int32, c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p,
+                                 c.c_int32, c.c_int32, c.c_int32, c.c_int32, c.c_float, c.c_void_p, c.c_void_p,
+                                 c.c_void_p]
     got, want = lib.vfa_abi_version(), _header_abi_version()
     if got != want:
         raise RuntimeError(f"{path} has ABI version {got}, include/vfa.h expects {want}: stale library")
@@ -350,3 +356,39 @@ def paged_attn_decode(q, k_cache, v_cache, block_table, cu_seqlens_q, seqused_k,
     if st != 0:
         raise VfaError(st, "paged_attn_decode")
     return out, lse
+
+
+def qk_norm_rope(q, k, q_weight, k_weight, cos, sin, eps: float = 1e-6, q_out=None, k_out=None):
+    """Per-head RMSNorm of q [T, Hq, D] and k [T, Hkv, D] (bf16) with bf16 weights [D], then the rotary
+    embedding with fp32 cos / sin [T, D]. Returns (q_out, k_out); pass q_out=q, k_out=k to work in place."""
+    torch = _torch()
+    lib = load_library()
+    _check_gpu("q", q, 3)
+    _check_gpu("k", k, 3)
+    for name, t in (("q_weight", q_weight), ("k_weight", k_weight)):
+        _check_gpu(name, t, 1)
+    for name, t in (("cos", cos), ("sin", sin)):
+        _check_gpu(name, t, 2)
+        if t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32")
+    if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16:
+        raise TypeError("q and k must be bfloat16")
+    if q_weight.dtype != torch.bfloat16 or k_weight.dtype != torch.bfloat16:
+        raise TypeError("q_weight and k_weight must be bfloat16")
+    t, hq, d = (int(x) for x in q.shape)
+    if int(k.shape[0]) != t or int(k.shape[2]) != d:
+        raise ValueError("q and k must share the token count and head_dim")
+    if tuple(cos.shape) != (t, d) or tuple(sin.shape) != (t, d):
+        raise ValueError(f"cos and sin must be [{t}, {d}]")
+    if q_out is None:
+        q_out = torch.empty_like(q)
+    if k_out is None:
+        k_out = torch.empty_like(k)
+    _check_gpu("q_out", q_out, 3)
+    _check_gpu("k_out", k_out, 3)
+    st = lib.qk_norm_rope(q.data_ptr(), k.data_ptr(), VFA_BF16, q_weight.data_ptr(), k_weight.data_ptr(),
+                          cos.data_ptr(), sin.data_ptr(), t, hq, int(k.shape[1]), d, float(eps), q_out.data_ptr(),
+                          k_out.data_ptr(), _stream_ptr(q.device))
+    if st != 0:
+        raise VfaError(st, "qk_norm_rope")
+    return q_out, k_out

@@ -272,3 +272,26 @@ VFA_API int32_t paged_attn_decode(const void* q, int32_t in_dtype, const void* k
   a.workspace = workspace; a.workspace_bytes = workspace_bytes; a.stream = stream;
   return vfa::launch_paged_decode_bf16(a, plan) == 0 ? VFA_OK : VFA_ERR_LAUNCH;
 }
+
+VFA_API int32_t qk_norm_rope(const void* q_in, const void* k_in, int32_t dtype, const void* q_weight,
+                             const void* k_weight, const float* cos, const float* sin, int32_t total_tokens,
+                             int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim, float eps, void* q_out,
+                             void* k_out, void* stream) {
+  if (total_tokens < 0 || num_heads_q < 0 || num_heads_kv < 0) return VFA_ERR_SHAPE;
+  if (total_tokens == 0 || num_heads_q + num_heads_kv == 0) return VFA_OK;
+  if (!cos || !sin) return VFA_ERR_NULL;
+  if (num_heads_q > 0 && (!q_in || !q_weight || !q_out)) return VFA_ERR_NULL;
+  if (num_heads_kv > 0 && (!k_in || !k_weight || !k_out)) return VFA_ERR_NULL;
+  if (head_dim != 64 && head_dim != 128) return VFA_ERR_UNSUPPORTED;
+  if (dtype != VFA_BF16) return VFA_ERR_UNSUPPORTED;
+  if (!std::isfinite(eps) || eps < 0.f) return VFA_ERR_UNSUPPORTED;
+  const void* ptrs[] = {q_in, k_in, q_weight, k_weight, q_out, k_out};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return VFA_ERR_UNSUPPORTED;
+  if (!aligned16(cos) || !aligned16(sin)) return VFA_ERR_UNSUPPORTED;
+  vfa::QkNormRopeArgs a{};
+  a.q_in = q_in; a.k_in = k_in; a.q_weight = q_weight; a.k_weight = k_weight; a.cos = cos; a.sin = sin;
+  a.tokens = total_tokens; a.hq = num_heads_q; a.hkv = num_heads_kv; a.head_dim = head_dim; a.eps = eps;
+  a.q_out = q_out; a.k_out = k_out; a.stream = stream;
+  return vfa::launch_qk_norm_rope(a) == 0 ? VFA_OK : VFA_ERR_LAUNCH;
+}

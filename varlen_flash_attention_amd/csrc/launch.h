@@ -68,6 +68,22 @@ struct PagedPlan {
 };
 PagedPlan plan_paged(int batch, int total_q, int max_seqlen_q, int max_seqlen_k, int hq, int hkv, int head_dim);
 
+// Attention prologue: per-head RMSNorm of q [tokens, hq, D] and k [tokens, hkv, D]
+// (bf16, weights bf16 [D]) then the rotary embedding with fp32 cos / sin [tokens, D].
+struct QkNormRopeArgs {
+  const void* q_in;
+  const void* k_in;
+  const void* q_weight;
+  const void* k_weight;
+  const float* cos;
+  const float* sin;
+  int tokens, hq, hkv, head_dim;
+  float eps;
+  void* q_out;
+  void* k_out;
+  void* stream;
+};
+
 // Each returns 0 on success, -1 if the HIP runtime reported a launch error.
 int launch_attn_fwd_bf16(const AttnArgs& a);
 int launch_attn_decode_bf16(const AttnArgs& a, const DecodePlan& plan);
@@ -75,6 +91,7 @@ int launch_attn_fwd_f32(const AttnArgs& a);
 int launch_paged_decode_bf16(const PagedArgs& a, const PagedPlan& plan);
 int launch_attn_update(const float* lse, const void* go, int go_dtype, int sp, int64_t bsh, int hd,
                        int update_type, void* out, float* lse_out, void* stream);
+int launch_qk_norm_rope(const QkNormRopeArgs& a);
 int launch_last_token_gather(const void* x, int esize, const int32_t* cu, int batch, int64_t row_elems,
                              void* out, void* stream);
 

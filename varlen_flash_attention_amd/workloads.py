@@ -39,6 +39,8 @@ __all__ = [
     "chunk_bounds",
     "PagedCache",
     "make_paged",
+    "PrologueInputs",
+    "make_prologue",
     "WORKLOAD_NAMES",
 ]
 
@@ -332,3 +334,47 @@ def make_paged(w: Workload, page_size: int, seed: int = 0, spare_pages: int = 3)
         cache[~filled] = round_to_bf16(junk, inplace=True) if w.dtype == "bf16" else junk
     return PagedCache(page_size=int(page_size), k_cache=k_cache, v_cache=v_cache, block_table=table,
                       seqused_k=lk.astype(np.int32))
+
+
+@dataclass
+class PrologueInputs:
+    """Inputs of the attention prologue (per-head q/k RMSNorm, then the rotary embedding)."""
+    lengths: np.ndarray                            # int64 [B]
+    q: np.ndarray = field(repr=False)              # bf16 values in fp32 [T, Hq, D]
+    k: np.ndarray = field(repr=False)              # bf16 values in fp32 [T, Hkv, D]
+    q_weight: np.ndarray = field(repr=False)       # bf16 values in fp32 [D]
+    k_weight: np.ndarray = field(repr=False)
+    cos: np.ndarray = field(repr=False)            # fp32 [T, D]
+    sin: np.ndarray = field(repr=False)
+    eps: float = 1e-6
+
+    @property
+    def cu_seqlens(self) -> np.ndarray:
+        return np.concatenate([[0], np.cumsum(self.lengths)]).astype(np.int32)
+
+
+def make_prologue(lengths, num_heads_q=32, num_heads_kv=8, head_dim=128, theta=1.0e6, eps=1e-6,
+                  seed=0) -> PrologueInputs:
+    """Seeded prologue inputs for packed sequences.
+
+    q and k are N(0, 4) (projection outputs are not unit scale; the norm
+    removes the scale), rounded to bf16; the weights are 1 + N(0, 0.01),
+    rounded to bf16. cos / sin rows follow the usual rotary tables: token i of
+    a sequence (positions restart at 0 in each sequence, as TND packs whole
+    sequences) at frequency j < D/2 has angle i * theta^(-2j/D), used for
+    both element j and element j + D/2; computed in fp64, stored fp32.
+    theta = 1e6 is the Qwen3 family's base.
+    """
+    lens = np.asarray(lengths, dtype=np.int64).reshape(-1)
+    t = int(lens.sum())
+    sq, sk, sw = np.random.SeedSequence(seed).spawn(3)
+    q = round_to_bf16(2.0 * _normal(sq, (t, num_heads_q, head_dim)), inplace=True)
+    k = round_to_bf16(2.0 * _normal(sk, (t, num_heads_kv, head_dim)), inplace=True)
+    w = round_to_bf16(1.0 + 0.1 * _normal(sw, (2, head_dim)), inplace=True)
+    pos = np.concatenate([np.arange(int(n), dtype=np.float64) for n in lens]) if t else np.zeros(0)
+    inv_freq = theta ** (-np.arange(0, head_dim, 2, dtype=np.float64) / head_dim)
+    ang = pos[:, None] * inv_freq[None, :]
+    ang = np.concatenate([ang, ang], axis=1)
+    return PrologueInputs(lengths=lens, q=q, k=k, q_weight=np.ascontiguousarray(w[0]),
+                          k_weight=np.ascontiguousarray(w[1]), cos=np.cos(ang).astype(np.float32),
+                          sin=np.sin(ang).astype(np.float32), eps=float(eps))
