@@ -26,8 +26,9 @@
 //                   read feeding NQ MFMAs), B = P^T converted to bf16 in
 //                   registers.
 // The QK of the next sub-block is issued before the softmax of the current
-// one. K and V stream through LDS with one barrier per 64 keys (see the
-// pipeline comment in the kernel).
+// one. K and V stream through LDS in tiles of BN keys with one barrier per
+// tile (see the pipeline comment in the kernel): 128 for the 8-wave shape,
+// 64 for the 4-wave shape, whose two workgroups per CU must share the LDS.
 #include <type_traits>
 
 #include "common.h"
@@ -40,7 +41,6 @@
 namespace vfa {
 namespace {
 
-constexpr int kBN = 64;              // keys per tile (V buffer / barrier period)
 constexpr int kXcds = 8;             // MI355X: 8 XCDs, blocks dispatched round-robin
 
 // Workgroup shapes: WAVES waves of NQ x 32 query columns each.
@@ -61,14 +61,14 @@ struct Shape {
 // LDS row strides, chosen from measured bank behaviour on gfx950: a 16-byte pad
 // makes the per-lane-row ds_read_b128 of K conflict-free; a 64-byte pad makes
 // the ds_read_b64_tr_b16 of V conflict-free (a 32-byte pad costs 2x).
-template <int D, int THREADS>
+template <int D, int THREADS, int BN>
 struct Smem {
   static constexpr int KSTR = D * 2 + 16;
   static constexpr int VSTR = D * 2 + 64;
-  static constexpr int KBYTES = kBN * KSTR;
-  static constexpr int VBYTES = kBN * VSTR;
+  static constexpr int KBYTES = BN * KSTR;
+  static constexpr int VBYTES = BN * VSTR;
   static constexpr int TOTAL = 2 * (KBYTES + VBYTES);
-  static constexpr int CHUNKS = kBN * D / 8;          // 16-byte chunks per tile (per tensor)
+  static constexpr int CHUNKS = BN * D / 8;           // 16-byte chunks per tile (per tensor)
   static constexpr int PER_THREAD = CHUNKS / THREADS;
   static_assert(CHUNKS % THREADS == 0, "tile must split evenly over the workgroup");
 };
@@ -85,7 +85,7 @@ __device__ __forceinline__ bf16x8 lds_read_tr_pair(const char VFA_LDS* p0, const
   return __builtin_bit_cast(bf16x8, r);
 }
 
-template <int WAVES, int NQ, int D, bool CAUSAL, typename OutT>
+template <int WAVES, int NQ, int D, bool CAUSAL, typename OutT, int BN>
 __global__ __attribute__((amdgpu_flat_work_group_size(1, Shape<WAVES, NQ>::THREADS),
                           amdgpu_waves_per_eu(Shape<WAVES, NQ>::WAVES_PER_EU, Shape<WAVES, NQ>::WAVES_PER_EU))) void
 attn_fwd_bf16_kernel(
@@ -94,11 +94,13 @@ attn_fwd_bf16_kernel(
     int batch, int hq, int hkv, int grp, int tokw, int n_mtiles, float scale, float scale_log2,
     OutT* __restrict__ out, float* __restrict__ lse) {
   constexpr int kThreads = Shape<WAVES, NQ>::THREADS;
-  using S = Smem<D, kThreads>;
+  using S = Smem<D, kThreads, BN>;
+  constexpr int kBN = BN;
+  constexpr int SUBS = BN / 32;                   // 32-key sub-blocks per tile
   __shared__ __attribute__((aligned(16))) char smem[S::TOTAL];
   char VFA_LDS* lds = (char VFA_LDS*)smem;
-  char VFA_LDS* kbufs = lds;                      // four 32-key K slots
-  char VFA_LDS* vbufs = lds + 2 * S::KBYTES;      // two 64-key V tiles
+  char VFA_LDS* kbufs = lds;                      // 2 * SUBS 32-key K slots
+  char VFA_LDS* vbufs = lds + 2 * S::KBYTES;      // two BN-key V tiles
 
   // Block -> work. Consecutive block ids go round-robin to the 8 XCDs, each
   // with its own L2. XCD x takes the (sequence, kv head) pairs x, x + 8, ...
@@ -169,7 +171,7 @@ attn_fwd_bf16_kernel(
   const int st_c8 = (tid % (D / 8)) * 8;
   constexpr int KEYS_PER_PASS = kThreads / (D / 8);
   // Sequence bases are wave-uniform; each lane adds fixed 32-bit byte offsets
-  // (64 rows of hkv * D bf16 stay far below 4 GiB), so a tile that lies wholly
+  // (BN rows of hkv * D bf16 stay far below 4 GiB), so a tile that lies wholly
   // inside the sequence needs no per-lane address arithmetic. Only the tail
   // tile clamps rows one by one.
   const char* kbase = (const char*)(k + ((size_t)k0 * hkv + g) * D);
@@ -179,7 +181,7 @@ attn_fwd_bf16_kernel(
 #pragma unroll
   for (int i = 0; i < S::PER_THREAD; ++i)
     st_off[i] = (uint32_t)((st_key + i * KEYS_PER_PASS) * row_bytes + st_c8 * sizeof(bf16));
-  // 64 consecutive keys starting at key0.
+  // BN consecutive keys starting at key0.
   auto gload = [&](u32x4 (&dst)[S::PER_THREAD], const char* base, int key0) {
     if (key0 + kBN <= lk) {
       const char* tile = base + (size_t)key0 * row_bytes;
@@ -193,15 +195,15 @@ attn_fwd_bf16_kernel(
       }
     }
   };
-  // V: one 64-key tile per buffer.
+  // V: one BN-key tile per buffer.
   auto sstore_v = [&](const u32x4 (&src)[S::PER_THREAD], char VFA_LDS* buf) {
 #pragma unroll
     for (int i = 0; i < S::PER_THREAD; ++i)
       *(u32x4 VFA_LDS*)(buf + (st_key + i * KEYS_PER_PASS) * S::VSTR + st_c8 * 2) = src[i];
   };
-  // K: a ring of four 32-key slots; sub-block n lives in slot n % 4. Stores
-  // 64 keys = sub-blocks (sub0, sub0 + 1).
-  auto k_slot = [&](int sub) { return kbufs + (sub & 3) * (32 * S::KSTR); };
+  // K: a ring of 2 * SUBS 32-key slots; sub-block n lives in slot
+  // n % (2 * SUBS). Stores BN keys = sub-blocks sub0 .. sub0 + SUBS-1.
+  auto k_slot = [&](int sub) { return kbufs + (sub & (2 * SUBS - 1)) * (32 * S::KSTR); };
   auto sstore_k = [&](const u32x4 (&src)[S::PER_THREAD], int sub0) {
 #pragma unroll
     for (int i = 0; i < S::PER_THREAD; ++i) {
@@ -256,7 +258,7 @@ attn_fwd_bf16_kernel(
   // recomputes. This drops the per-block max from the common path.
   constexpr float kSumLimit = 4294967296.f;
 
-  // Softmax and PV for sub-block sb of tile j (keys j*64 + sb*32 ...).
+  // Softmax and PV for sub-block sb of tile j (keys j*BN + sb*32 ...).
   auto softmax_pv = [&](auto masked, f32x16 (&s)[NQ], int j, int sb) {
     if constexpr (decltype(masked)::value) {
 #pragma unroll
@@ -335,43 +337,48 @@ attn_fwd_bf16_kernel(
     }
   };
 
-  // Pipeline. Iteration j does softmax + PV for sub-blocks 2j and 2j+1 (V
-  // tile j) and the QK of sub-blocks 2j+1 and 2j+2, each QK issued before the
-  // previous sub-block's softmax. It refills the two K slots freed by the
-  // previous iteration with sub-blocks 2j+3, 2j+4 and V buffer (j+1)%2 with V
-  // tile j+1 (loaded into registers one iteration earlier), so one barrier per
-  // iteration separates every LDS write from the reads of the same slot.
-  const int n_sub = 2 * n_tiles;
+  // Pipeline (SUBS = BN / 32 sub-blocks per tile). Iteration j does softmax +
+  // PV for sub-blocks SUBS*j .. SUBS*j + SUBS-1 (V tile j) and the QK of
+  // sub-blocks SUBS*j + 1 .. SUBS*j + SUBS, each QK issued before the previous
+  // sub-block's softmax. It refills the SUBS K slots freed by the previous
+  // iteration (whose QKs it ran) with sub-blocks SUBS*j + SUBS+1 ..
+  // SUBS*j + 2*SUBS, and V buffer (j+1)%2 with V tile j+1 (both loaded into
+  // registers one iteration earlier), so one barrier per iteration separates
+  // every LDS write from the reads of the same slot.
+  const int n_sub = SUBS * n_tiles;
+  const int n_sub_vis = (n_end + 31) / 32;         // sub-blocks holding a visible key
   if (n_tiles > 0) {
     // All three first loads in flight together (one memory round trip).
     u32x4 kst2[S::PER_THREAD];
     gload(kst, kbase, 0);
     gload(vst, vbase, 0);
-    gload(kst2, kbase, 64);
+    gload(kst2, kbase, kBN);
     sstore_k(kst, 0);
     sstore_v(vst, vbufs);
-    sstore_k(kst2, 2);
+    sstore_k(kst2, SUBS);
   }
   __syncthreads();
-  if (n_sub > 3) gload(kst, kbase, 3 * 32);
+  if (n_sub > SUBS + 1) gload(kst, kbase, (SUBS + 1) * 32);
   if (n_tiles > 1) gload(vst, vbase, kBN);
   f32x16 s_cur[NQ], s_next[NQ];
   qk(0, s_cur);
 
   auto tile_step = [&](auto masked, int j) {
     __syncthreads();
-    if (2 * j + 3 < n_sub) sstore_k(kst, 2 * j + 3);
+    if (SUBS * j + SUBS + 1 < n_sub) sstore_k(kst, SUBS * j + SUBS + 1);
     if (j + 1 < n_tiles) sstore_v(vst, vbufs + ((j + 1) & 1) * S::VBYTES);
-    if (2 * j + 5 < n_sub) gload(kst, kbase, (2 * j + 5) * 32);
+    if (SUBS * j + 2 * SUBS + 1 < n_sub) gload(kst, kbase, (SUBS * j + 2 * SUBS + 1) * 32);
     if (j + 2 < n_tiles) gload(vst, vbase, (j + 2) * kBN);
-    qk(2 * j + 1, s_next);
-    softmax_pv(masked, s_cur, j, 0);
 #pragma unroll
-    for (int qb = 0; qb < NQ; ++qb) s_cur[qb] = s_next[qb];
-    qk(2 * j + 2, s_next);     // stale slot after the last tile: computed, never used
-    softmax_pv(masked, s_cur, j, 1);
+    for (int sb = 0; sb < SUBS; ++sb) {
+      // Masked tiles: sub-blocks wholly past the block's last visible key hold
+      // nothing for any row (n_sub_vis is uniform over the workgroup).
+      if (decltype(masked)::value && SUBS * j + sb >= n_sub_vis) break;
+      qk(SUBS * j + sb + 1, s_next);   // the last one of the last tile reads a stale slot: computed, never used
+      softmax_pv(masked, s_cur, j, sb);
 #pragma unroll
-    for (int qb = 0; qb < NQ; ++qb) s_cur[qb] = s_next[qb];
+      for (int qb = 0; qb < NQ; ++qb) s_cur[qb] = s_next[qb];
+    }
   };
   int j = 0;
   for (; j < j_full; ++j) tile_step(std::integral_constant<bool, false>{}, j);
@@ -422,13 +429,14 @@ attn_fwd_bf16_kernel(
 
 template <int WAVES, int NQ, int D, bool CAUSAL, typename OutT>
 int launch_t(const AttnArgs& a) {
+  constexpr int BN = WAVES == 8 ? 128 : 64;
   const int tokw = Shape<WAVES, NQ>::COLS / a.grp;
   const int n_mtiles = (a.max_seqlen_q + tokw - 1) / tokw;
   const long long pairs_per_xcd = ((long long)a.batch * a.hkv + kXcds - 1) / kXcds;
   const long long blocks = (long long)n_mtiles * pairs_per_xcd * kXcds;
   if (blocks <= 0) return 0;
   if (blocks > 0x7fffffffLL) return -1;
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<WAVES, NQ, D, CAUSAL, OutT>), dim3((unsigned)blocks),
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<WAVES, NQ, D, CAUSAL, OutT, BN>), dim3((unsigned)blocks),
                      dim3(Shape<WAVES, NQ>::THREADS), 0, (hipStream_t)a.stream, (const bf16*)a.q,
                      (const bf16*)a.k, (const bf16*)a.v, a.cu_q, a.cu_k, a.causal_off, a.batch, a.hq, a.hkv,
                      a.grp, tokw, n_mtiles, a.scale, a.scale * kLog2e, (OutT*)a.out, a.lse);
