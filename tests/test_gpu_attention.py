@@ -164,6 +164,18 @@ def test_decode_variants(hq, hkv, lq, d, causal):
     full_check(f"decode Hq={hq} Hkv={hkv} Lq={lq} D={d} causal={causal}", w)
 
 
+@pytest.mark.parametrize("lk,hq,hkv", [
+    ([12800, 300, 9000], 16, 2),       # 50 splits of 256 keys: the combine's 64-partial register path
+    ([70000, 17, 40000], 8, 1),        # 274 splits: the combine's streaming loop
+])
+def test_decode_many_splits(lk, hq, hkv):
+    w = make_custom([1] * len(lk), lk, num_heads_q=hq, num_heads_kv=hkv, head_dim=128, dtype="bf16", causal=True,
+                    seed=110 + len(lk) + hkv)
+    ws = vfa.varlen_attn_fwd_workspace_size(w.batch, w.total_q, w.max_seqlen_q, w.max_seqlen_k, hq, hkv, 128)
+    print(f"[case] decode many splits lk={lk} workspace={ws}", flush=True)
+    full_check(f"decode_many_splits lk={lk}", w)
+
+
 def test_loose_max_seqlen_bounds():
     w = make_custom([40, 129, 7], num_heads_q=8, num_heads_kv=2, head_dim=128, dtype="bf16", causal=True, seed=100)
     print("[case] loose max_seqlen bounds", flush=True)

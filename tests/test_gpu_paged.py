@@ -131,6 +131,9 @@ def test_paged_deterministic():
     a = run_paged(w, pc, d=d)
     b = run_paged(w, pc, d=d)
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    # 79 splits of 256 keys: the combine's streaming loop, against the oracle too
+    o_ref, l_ref = run_oracle(w, pc)
+    check("paged_deterministic", host64(a[0]), host64(a[1]), o_ref, l_ref, "bf16")
 
 
 def test_paged_debug_check(monkeypatch):
