@@ -25,6 +25,11 @@ Parity status per function (what pins it; see tests/test_oracle_*.py):
       (tests/golden/qk_norm_rope_handworked.json), torch's fp64 rms_norm,
       the rotation as complex multiplication by exp(i theta), identity at
       position 0, and the pair norms it preserves.
+  linear_attention.gated_delta_rule -- pinned: a hand-worked overwrite
+      (tests/golden/gated_delta_handworked.json), beta = 0 closed form,
+      orthonormal-key associative recall, continuation through the state,
+      packed == per sequence, linearity in v, and an independently written
+      chunked (WY) formulation.
 """
 from .attention import (  # noqa: F401
     varlen_attention,
@@ -41,3 +46,4 @@ from .prologue import (  # noqa: F401
     rotary,
     qk_norm_rope,
 )
+from .linear_attention import gated_delta_rule  # noqa: F401

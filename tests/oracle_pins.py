@@ -530,3 +530,138 @@ PROLOGUE_CHECKS = [
     check_rotary_identity_and_pair_norms,
     check_rms_norm_invariants,
 ]
+
+
+# ------------------------------------------------------------------ gated delta rule (oracle/linear_attention.py)
+
+def _gdn_inputs(rng, lengths, hqk, hv, dk, dv, decay=(0.8, 1.0)):
+    t = int(sum(lengths))
+    q = rng.standard_normal((t, hqk, dk))
+    k = rng.standard_normal((t, hqk, dk))
+    q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((t, hv, dv))
+    g = np.log(rng.uniform(decay[0], decay[1], (t, hv)))
+    beta = rng.uniform(0.0, 1.0, (t, hv))
+    return q, k, v, g, beta
+
+
+def check_golden_gated_delta(lin):
+    gd = _load("gated_delta_handworked.json")
+    q = np.array(gd["q"], dtype=np.float64)[:, None, :]
+    k = np.array(gd["k"], dtype=np.float64)[:, None, :]
+    v = np.array(gd["v"], dtype=np.float64)[:, None, :]
+    g = np.log(np.array(gd["decay"], dtype=np.float64))[:, None]
+    beta = np.array(gd["beta"], dtype=np.float64)[:, None]
+    o, fin = lin.gated_delta_rule(q, k, v, g, beta, [0, 3], 1.0)
+    assert np.allclose(o[:, 0, :], np.array(gd["out"], dtype=np.float64), rtol=1e-14, atol=1e-14), o
+    assert np.allclose(fin[0, 0], np.array(gd["final_state"], dtype=np.float64), rtol=1e-14, atol=1e-14), fin
+
+
+def check_gated_delta_beta_zero(lin, seed=43):
+    """beta = 0: nothing is written, so the state is the decayed initial state and
+    o_t = scale * (prod_{s<=t} a_s) * S0^T q_t."""
+    rng = np.random.default_rng(seed)
+    q, k, v, g, _ = _gdn_inputs(rng, [5, 3], 2, 4, 6, 5)
+    s0 = rng.standard_normal((2, 4, 6, 5))
+    o, fin = lin.gated_delta_rule(q, k, v, g, np.zeros_like(g), [0, 5, 8], 0.7, initial_state=s0)
+    for b, (lo, hi) in enumerate(((0, 5), (5, 8))):
+        for h in range(4):
+            cum = np.exp(np.cumsum(g[lo:hi, h]))
+            want = 0.7 * cum[:, None] * (q[lo:hi, h // 2] @ s0[b, h])
+            assert np.allclose(o[lo:hi, h], want, rtol=1e-12, atol=1e-12)
+            assert np.allclose(fin[b, h], cum[-1] * s0[b, h], rtol=1e-12, atol=1e-12)
+
+
+def check_gated_delta_associative_recall(lin, seed=47):
+    """No decay, beta = 1, keys the standard basis vectors e_0, e_1, ...: each write lands in an empty
+    slot, so querying with e_r after token r returns scale * v_r exactly."""
+    rng = np.random.default_rng(seed)
+    dk, dv, t = 8, 3, 6
+    k = np.eye(dk)[:t][:, None, :]
+    v = rng.standard_normal((t, 1, dv))
+    r = [0, 1, 0, 3, 2, 4]                               # query slot <= token index
+    q = np.eye(dk)[r][:, None, :]
+    o, _ = lin.gated_delta_rule(q, k, v, np.zeros((t, 1)), np.ones((t, 1)), [0, t], 1.5)
+    assert np.allclose(o[:, 0, :], 1.5 * v[r, 0, :], rtol=1e-14, atol=1e-14)
+
+
+def check_gated_delta_continuation_and_packing(lin, seed=53):
+    """Running a sequence in two pieces, the second started from the first's final state, equals running
+    it whole; a packed batch equals its sequences run one by one."""
+    rng = np.random.default_rng(seed)
+    q, k, v, g, beta = _gdn_inputs(rng, [9, 4, 7], 1, 2, 4, 3)
+    o_all, fin_all = lin.gated_delta_rule(q, k, v, g, beta, [0, 9, 13, 20], 0.5)
+    for b, (lo, hi) in enumerate(((0, 9), (9, 13), (13, 20))):
+        o_b, fin_b = lin.gated_delta_rule(q[lo:hi], k[lo:hi], v[lo:hi], g[lo:hi], beta[lo:hi], [0, hi - lo], 0.5)
+        assert np.allclose(o_b, o_all[lo:hi], rtol=1e-13, atol=1e-13)
+        assert np.allclose(fin_b[0], fin_all[b], rtol=1e-13, atol=1e-13)
+    lo, mid, hi = 0, 5, 9
+    o1, f1 = lin.gated_delta_rule(q[lo:mid], k[lo:mid], v[lo:mid], g[lo:mid], beta[lo:mid], [0, mid], 0.5)
+    o2, f2 = lin.gated_delta_rule(q[mid:hi], k[mid:hi], v[mid:hi], g[mid:hi], beta[mid:hi], [0, hi - mid], 0.5,
+                                  initial_state=f1)
+    assert np.allclose(np.concatenate([o1, o2]), o_all[lo:hi], rtol=1e-13, atol=1e-13)
+    assert np.allclose(f2[0], fin_all[0], rtol=1e-13, atol=1e-13)
+
+
+def check_gated_delta_linear_in_v(lin, seed=59):
+    rng = np.random.default_rng(seed)
+    q, k, v, g, beta = _gdn_inputs(rng, [6, 5], 2, 2, 5, 4)
+    v2 = rng.standard_normal(v.shape)
+    cu = [0, 6, 11]
+    a, fa = lin.gated_delta_rule(q, k, v, g, beta, cu, 1.0)
+    b, fb = lin.gated_delta_rule(q, k, v2, g, beta, cu, 1.0)
+    c, fc = lin.gated_delta_rule(q, k, 2.0 * v - v2, g, beta, cu, 1.0)
+    assert np.allclose(c, 2.0 * a - b, rtol=1e-12, atol=1e-12)
+    assert np.allclose(fc, 2.0 * fa - fb, rtol=1e-12, atol=1e-12)
+
+
+def _gdn_chunked(q, k, v, g, beta, cu, scale, chunk):
+    """The same operator written the chunked (WY) way: per chunk, the corrections of all its tokens come
+    from one lower-triangular solve, outputs and the state update from matrix products."""
+    t_all, hqk, dk = q.shape
+    hv, dv = v.shape[1], v.shape[2]
+    rep = hv // hqk
+    out = np.zeros((t_all, hv, dv))
+    fin = np.zeros((len(cu) - 1, hv, dk, dv))
+    for b in range(len(cu) - 1):
+        for h in range(hv):
+            st = np.zeros((dk, dv))
+            for c0 in range(cu[b], cu[b + 1], chunk):
+                c1 = min(c0 + chunk, cu[b + 1])
+                kc, qc, vc = k[c0:c1, h // rep], q[c0:c1, h // rep], v[c0:c1, h]
+                gcum = np.cumsum(g[c0:c1, h])
+                bc = beta[c0:c1, h]
+                decay = np.exp(gcum[:, None] - gcum[None, :])
+                n = c1 - c0
+                strict = np.tril(np.ones((n, n)), -1)
+                incl = np.tril(np.ones((n, n)))
+                lmat = strict * decay * (kc @ kc.T)
+                rhs = bc[:, None] * (vc - np.exp(gcum)[:, None] * (kc @ st))
+                u = np.linalg.solve(np.eye(n) + bc[:, None] * lmat, rhs)
+                out[c0:c1, h] = scale * (np.exp(gcum)[:, None] * (qc @ st) + (incl * decay * (qc @ kc.T)) @ u)
+                st = np.exp(gcum[-1]) * st + kc.T @ (np.exp(gcum[-1] - gcum)[:, None] * u)
+            fin[b, h] = st
+    return out, fin
+
+
+def check_gated_delta_chunked_form(lin, seed=61):
+    rng = np.random.default_rng(seed)
+    lens = [13, 1, 20, 8]
+    q, k, v, g, beta = _gdn_inputs(rng, lens, 2, 4, 6, 5, decay=(0.5, 1.0))
+    cu = [0, 13, 14, 34, 42]
+    o, fin = lin.gated_delta_rule(q, k, v, g, beta, cu, 0.4)
+    for chunk in (1, 4, 7, 64):
+        oc, fc = _gdn_chunked(q, k, v, g, beta, cu, 0.4, chunk)
+        assert np.allclose(oc, o, rtol=1e-11, atol=1e-11), chunk
+        assert np.allclose(fc, fin, rtol=1e-11, atol=1e-11), chunk
+
+
+GDN_CHECKS = [
+    check_golden_gated_delta,
+    check_gated_delta_beta_zero,
+    check_gated_delta_associative_recall,
+    check_gated_delta_continuation_and_packing,
+    check_gated_delta_linear_in_v,
+    check_gated_delta_chunked_form,
+]

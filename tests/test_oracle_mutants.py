@@ -14,6 +14,7 @@ from tests import oracle_pins as pins
 ORACLE_DIR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle")
 SRC = os.path.join(ORACLE_DIR, "attention.py")
 PROLOGUE_SRC = os.path.join(ORACLE_DIR, "prologue.py")
+LINEAR_SRC = os.path.join(ORACLE_DIR, "linear_attention.py")
 
 MUTANTS = {
     "gqa_modulo_mapping": ("g = h // grp", "g = h % hkv"),
@@ -55,6 +56,19 @@ PROLOGUE_MUTANTS = {
     "rms_eps_outside_sqrt": ("x / np.sqrt(var + eps)", "x / (np.sqrt(var) + eps)"),
     "rms_weight_dropped": ("* np.asarray(weight, dtype=np.float64)", "* 1.0"),
     "k_takes_q_weight": ("rotary(rms_norm(k, k_weight, eps), cos, sin)", "rotary(rms_norm(k, q_weight, eps), cos, sin)"),
+}
+
+
+GDN_MUTANTS = {
+    "decay_after_correction": ("s = np.exp(g[t, h]) * s\n                u = beta[t, h] * (v[t, h] - s.T @ k[t, hk])",
+                               "u = beta[t, h] * (v[t, h] - s.T @ k[t, hk])\n                s = np.exp(g[t, h]) * s"),
+    "beta_dropped": ("u = beta[t, h] * (v[t, h] - s.T @ k[t, hk])", "u = (v[t, h] - s.T @ k[t, hk])"),
+    "delta_sign": ("u = beta[t, h] * (v[t, h] - s.T @ k[t, hk])", "u = beta[t, h] * (v[t, h] + s.T @ k[t, hk])"),
+    "read_before_write": ("s = s + np.outer(k[t, hk], u)\n                out[t, h] = scale * (s.T @ q[t, hk])",
+                          "out[t, h] = scale * (s.T @ q[t, hk])\n                s = s + np.outer(k[t, hk], u)"),
+    "write_with_query": ("s = s + np.outer(k[t, hk], u)", "s = s + np.outer(q[t, hk], u)"),
+    "head_map_modulo": ("hk = h // rep", "hk = h % hqk"),
+    "state_not_reset": ("s = (np.zeros((dk, dv)) if initial_state is None", "s = (s if (b > 0 and initial_state is None) else np.zeros((dk, dv)) if initial_state is None"),
 }
 
 
@@ -101,3 +115,15 @@ def test_unmutated_prologue_passes():
     mod = _mutant_module("import numpy as np", "import numpy as np", path=PROLOGUE_SRC)
     for check in pins.PROLOGUE_CHECKS:
         check(mod)
+
+
+@pytest.mark.parametrize("name", sorted(GDN_MUTANTS))
+def test_gated_delta_mutant_is_caught(name):
+    mod = _mutant_module(*GDN_MUTANTS[name], path=LINEAR_SRC)
+    caught = []
+    for check in pins.GDN_CHECKS:
+        try:
+            check(mod)
+        except Exception as exc:  # noqa: BLE001 - any failure counts as caught
+            caught.append((check.__name__, type(exc).__name__))
+    assert caught, f"no pin catches gated delta mutant {name}"

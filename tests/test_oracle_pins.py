@@ -13,3 +13,8 @@ def test_oracle_pin(check):
 @pytest.mark.parametrize("check", pins.PROLOGUE_CHECKS, ids=lambda f: f.__name__)
 def test_prologue_pin(check):
     check(oracle.prologue)
+
+
+@pytest.mark.parametrize("check", pins.GDN_CHECKS, ids=lambda f: f.__name__)
+def test_gated_delta_pin(check):
+    check(oracle.linear_attention)
