@@ -12,9 +12,10 @@ head, key), masked pairs excluded. One JSON line is printed.
 Extra fields (not the headline): the embedding-style prefill with the
 last-token gather, the same long prefill without masking, decode against
 long KV sets (contiguous, and paged with 16- and 128-key pages), the q/k
-RMSNorm + rotary prologue on the long-prefill tokens, and the attn_update
-merge of the chunked-context config (sp=8, bsh=2048, hd=128,
-fp32) timed with caches flushed before every rep.
+RMSNorm + rotary prologue on the long-prefill tokens, the gated delta rule
+(linear attention) on the same lengths, and the attn_update merge of the
+chunked-context config (sp=8, bsh=2048, hd=128, fp32) timed with caches
+flushed before every rep.
 
 "roofline" is the attention kernel's achieved useful FLOP rate (per-launch
 HIP-event durations on the launch stream) against the bf16 dense MFMA peak;
@@ -186,6 +187,41 @@ def prologue_case(vfa, torch, lengths, reps=20, warmup=3):
            "gb_per_s": round(byt / t / 1e6, 1), "frac_hbm_peak": round(byt / t / 1e6 / PEAK_HBM_GBPS, 4),
            "tokens": tokens}
     del q, k, wq, wk, cos, sin, qo, ko
+    torch.cuda.empty_cache()
+    return res
+
+
+PEAK_FP32_VECTOR_TFLOPS = 157.3   # MI355X fp32 vector (256 CUs at 2.4 GHz)
+
+
+def gated_delta_case(vfa, torch, lengths, reps=5, warmup=1):
+    """gated_delta_rule_fwd on the long-prefill lengths with 16 query/key and 32 value heads, D 128.
+    Algorithmic FLOPs per (token, value head): 7 * Dk * Dv (S^T k, decay, rank-1 write, S^T q)."""
+    import numpy as np
+    from varlen_flash_attention_amd.workloads import bf16_bits, make_gated_delta
+
+    p = make_gated_delta(lengths, 16, 32, 128, 128, seed=93)
+
+    def dev(x):
+        return torch.from_numpy(bf16_bits(x).view(np.int16)).cuda().view(torch.bfloat16)
+
+    q, k, v = dev(p.q), dev(p.k), dev(p.v)
+    g, beta = torch.from_numpy(p.g).cuda(), torch.from_numpy(p.beta).cuda()
+    cu = torch.from_numpy(p.cu_seqlens).cuda()
+    out = torch.empty((int(p.lengths.sum()), 32, 128), dtype=torch.bfloat16, device="cuda")
+
+    def call():
+        vfa.gated_delta_rule_fwd(q, k, v, g, beta, cu, scale=p.scale, out=out)
+
+    ms = time_calls(call, reps, warmup, torch)
+    t = median(ms)
+    tokens = int(p.lengths.sum())
+    flops = 7.0 * 128 * 128 * 32 * tokens
+    res = {"ms_median": round(t, 4), "ms_p10": round(sorted(ms)[len(ms) // 10], 4),
+           "ms_p90": round(sorted(ms)[(9 * len(ms)) // 10], 4), "gflop": round(flops / 1e9, 2),
+           "tflops": round(flops / t / 1e9, 2), "frac_fp32_vector_peak": round(flops / t / 1e9 / PEAK_FP32_VECTOR_TFLOPS, 4),
+           "tokens": tokens, "longest_sequence": int(p.lengths.max())}
+    del q, k, v, g, beta, cu, out
     torch.cuda.empty_cache()
     return res
 
@@ -381,6 +417,8 @@ def main() -> int:
         del wd
         log("[bench] extra: q/k RMSNorm + rotary prologue")
         extra["qk_norm_rope"] = prologue_case(vfa, torch, w.lengths_q)
+        log("[bench] extra: gated delta rule (linear attention)")
+        extra["gated_delta_rule"] = gated_delta_case(vfa, torch, w.lengths_q)
         log("[bench] extra: attn_update merge")
         extra["attn_update_merge"] = merge_case(vfa, torch)
 

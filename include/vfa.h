@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define VFA_ABI_VERSION 4
+#define VFA_ABI_VERSION 5
 
 typedef enum vfa_status {
   VFA_OK = 0,
@@ -275,6 +275,39 @@ int32_t qk_norm_rope(const void* q_in, const void* k_in, int32_t dtype,
                      int32_t total_tokens, int32_t num_heads_q, int32_t num_heads_kv,
                      int32_t head_dim, float eps,
                      void* q_out, void* k_out, void* stream);
+
+/* Varlen gated delta rule forward: the linear-attention operator of the
+ * hybrid model on "Twinkle NPU kernels" (Qwen3.5 flash linear attention
+ * section: chunk_gated_delta_rule over packed sequences with cu_seqlens).
+ * The page names the operator only; the recurrence below is the reading
+ * taken. For every sequence b and value head h, with S [Dk, Dv] starting at
+ * initial_state[b, h] (or zero):
+ *   S   <- exp(g[t, h]) * S
+ *   u    = beta[t, h] * (v[t, h, :] - S^T k[t, h / R, :])        R = Hv / Hqk
+ *   S   <- S + k[t, h / R, :] u^T
+ *   out[t, h, :] = scale * S^T q[t, h / R, :]
+ * over the sequence's tokens in order; final_state[b, h] = S.
+ *
+ * q, k          [total_tokens, num_heads_qk, head_dim_k]   bf16
+ * v             [total_tokens, num_heads_v, head_dim_v]    bf16
+ * g, beta       [total_tokens, num_heads_v]                fp32
+ * cu_seqlens    device int32 [batch + 1], as for varlen_attn_fwd (caller
+ *               contract; checked on the device under VFA_DEBUG)
+ * initial_state [batch, num_heads_v, head_dim_k, head_dim_v] fp32, or NULL
+ * out           [total_tokens, num_heads_v, head_dim_v]    bf16
+ * final_state   [batch, num_heads_v, head_dim_k, head_dim_v] fp32, or NULL
+ * The state is kept and updated in fp32; out is rounded once to bf16.
+ * Supported: dtype VFA_BF16; head_dim_k and head_dim_v in {64, 128};
+ * num_heads_v a multiple of num_heads_qk; scale finite.
+ * batch == 0 returns VFA_OK.
+ */
+int32_t gated_delta_rule_fwd(const void* q, const void* k, const void* v, int32_t dtype,
+                             const float* g, const float* beta, const int32_t* cu_seqlens,
+                             int32_t batch, int32_t total_tokens,
+                             int32_t num_heads_qk, int32_t num_heads_v,
+                             int32_t head_dim_k, int32_t head_dim_v, float scale,
+                             const float* initial_state, void* out, float* final_state,
+                             void* stream);
 
 /* Last-token gather ([P1] core optimisation 1, embed(): x[cu_seqlens[1:] - 1]).
  *

@@ -44,7 +44,7 @@ def test_exports_match_header(lib):
 
 
 def test_abi_version(lib):
-    assert lib.vfa_abi_version() == vfa._header_abi_version() == 4
+    assert lib.vfa_abi_version() == vfa._header_abi_version() == 5
 
 
 def test_status_strings(lib):
@@ -264,3 +264,30 @@ def _qknr(lib, **kw):
 ])
 def test_qk_norm_rope_validation(lib, kw, code):
     assert _qknr(lib, **kw) == code
+
+
+def _gdn(lib, **kw):
+    a = dict(q=P, k=P, v=P, dtype=BF16, g=P, beta=P, cu=P, batch=2, t=16, hqk=16, hv=32, dk=128, dv=128,
+             scale=0.088, s0=None, out=P, s1=None, stream=None)
+    a.update(kw)
+    return lib.gated_delta_rule_fwd(a["q"], a["k"], a["v"], a["dtype"], a["g"], a["beta"], a["cu"], a["batch"],
+                                    a["t"], a["hqk"], a["hv"], a["dk"], a["dv"], a["scale"], a["s0"], a["out"],
+                                    a["s1"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=0), OK),
+    (dict(batch=-1), SHAPE),
+    (dict(hqk=0), SHAPE),
+    (dict(hqk=3, hv=32), SHAPE),             # Hv not a multiple of Hqk
+    (dict(q=None), NULL),
+    (dict(g=None), NULL),
+    (dict(cu=None), NULL),
+    (dict(out=None), NULL),
+    (dict(dtype=F32), UNSUP),
+    (dict(dk=96), UNSUP),
+    (dict(dv=32), UNSUP),
+    (dict(scale=float("inf")), UNSUP),
+])
+def test_gated_delta_validation(lib, kw, code):
+    assert _gdn(lib, **kw) == code

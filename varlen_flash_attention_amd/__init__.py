@@ -19,6 +19,8 @@ Entry points (same names as the C ABI in include/vfa.h):
                     max_seqlen_k, softmax_scale=None, causal=True, out_dtype=None) -> (out, lse)
   paged_attn_decode_workspace_size(...) -> bytes
   qk_norm_rope(q, k, q_weight, k_weight, cos, sin, eps=1e-6, q_out=None, k_out=None) -> (q_out, k_out)
+  gated_delta_rule_fwd(q, k, v, g, beta, cu_seqlens, scale=None, initial_state=None,
+                       output_final_state=False) -> (out, final_state or None)
 """
 from __future__ import annotations
 
@@ -40,6 +42,7 @@ __all__ = [
     "paged_attn_decode",
     "paged_attn_decode_workspace_size",
     "qk_norm_rope",
+    "gated_delta_rule_fwd",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -127,6 +130,10 @@ def load_library() -> ctypes.CDLL:
     lib.qk_norm_rope.argtypes = [c.c_void_p, c.c_void_p, c.c_int32, c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p,
                                  c.c_int32, c.c_int32, c.c_int32, c.c_int32, c.c_float, c.c_void_p, c.c_void_p,
                                  c.c_void_p]
+    lib.gated_delta_rule_fwd.restype = c.c_int32
+    lib.gated_delta_rule_fwd.argtypes = [c.c_void_p, c.c_void_p, c.c_void_p, c.c_int32, c.c_void_p, c.c_void_p,
+                                         c.c_void_p, c.c_int32, c.c_int32, c.c_int32, c.c_int32, c.c_int32,
+                                         c.c_int32, c.c_float, c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p]
     got, want = lib.vfa_abi_version(), _header_abi_version()
     if got != want:
         raise RuntimeError(f"{path} has ABI version {got}, include/vfa.h expects {want}: stale library")
@@ -392,3 +399,46 @@ def qk_norm_rope(q, k, q_weight, k_weight, cos, sin, eps: float = 1e-6, q_out=No
     if st != 0:
         raise VfaError(st, "qk_norm_rope")
     return q_out, k_out
+
+
+def gated_delta_rule_fwd(q, k, v, g, beta, cu_seqlens, scale: float | None = None, initial_state=None,
+                         output_final_state: bool = False, out=None):
+    """Varlen gated delta rule forward. q, k [T, Hqk, Dk] and v [T, Hv, Dv] bf16; g, beta [T, Hv] fp32;
+    cu_seqlens int32 [B+1]; initial_state [B, Hv, Dk, Dv] fp32 or None. Default scale 1/sqrt(Dk).
+    Returns (out [T, Hv, Dv] bf16, final_state [B, Hv, Dk, Dv] fp32 or None)."""
+    torch = _torch()
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_gpu(name, t, 3)
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"{name} must be bfloat16")
+    for name, t in (("g", g), ("beta", beta)):
+        _check_gpu(name, t, 2)
+        if t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32")
+    _check_gpu("cu_seqlens", cu_seqlens, 1)
+    if cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    tt, hqk, dk = (int(x) for x in q.shape)
+    hv, dv = int(v.shape[1]), int(v.shape[2])
+    if tuple(k.shape) != tuple(q.shape) or int(v.shape[0]) != tt:
+        raise ValueError("q and k must match, and v must have the same token count")
+    if tuple(g.shape) != (tt, hv) or tuple(beta.shape) != (tt, hv):
+        raise ValueError(f"g and beta must be [{tt}, {hv}]")
+    batch = int(cu_seqlens.shape[0]) - 1
+    if initial_state is not None:
+        _check_gpu("initial_state", initial_state, 4)
+        if initial_state.dtype != torch.float32 or tuple(initial_state.shape) != (batch, hv, dk, dv):
+            raise ValueError(f"initial_state must be float32 [{batch}, {hv}, {dk}, {dv}]")
+    if out is None:
+        out = torch.empty((tt, hv, dv), dtype=torch.bfloat16, device=q.device)
+    _check_gpu("out", out, 3)
+    final = torch.empty((batch, hv, dk, dv), dtype=torch.float32, device=q.device) if output_final_state else None
+    sc = 1.0 / math.sqrt(dk) if scale is None else float(scale)
+    st = lib.gated_delta_rule_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), VFA_BF16, g.data_ptr(), beta.data_ptr(),
+                                  cu_seqlens.data_ptr(), batch, tt, hqk, hv, dk, dv, sc,
+                                  initial_state.data_ptr() if initial_state is not None else None, out.data_ptr(),
+                                  final.data_ptr() if final is not None else None, _stream_ptr(q.device))
+    if st != 0:
+        raise VfaError(st, "gated_delta_rule_fwd")
+    return out, final

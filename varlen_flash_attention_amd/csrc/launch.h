@@ -84,6 +84,24 @@ struct QkNormRopeArgs {
   void* stream;
 };
 
+// Varlen gated delta rule forward: q, k [tokens, hqk, dk], v [tokens, hv, dv] bf16;
+// g, beta [tokens, hv] fp32; states [batch, hv, dk, dv] fp32 (optional); out
+// [tokens, hv, dv] bf16.
+struct GatedDeltaArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g;
+  const float* beta;
+  const int32_t* cu;
+  int batch, tokens, hqk, hv, dk, dv;
+  float scale;
+  const float* s_init;
+  void* out;
+  float* s_final;
+  void* stream;
+};
+
 // Each returns 0 on success, -1 if the HIP runtime reported a launch error.
 int launch_attn_fwd_bf16(const AttnArgs& a);
 int launch_attn_decode_bf16(const AttnArgs& a, const DecodePlan& plan);
@@ -92,6 +110,7 @@ int launch_paged_decode_bf16(const PagedArgs& a, const PagedPlan& plan);
 int launch_attn_update(const float* lse, const void* go, int go_dtype, int sp, int64_t bsh, int hd,
                        int update_type, void* out, float* lse_out, void* stream);
 int launch_qk_norm_rope(const QkNormRopeArgs& a);
+int launch_gated_delta(const GatedDeltaArgs& a);
 int launch_last_token_gather(const void* x, int esize, const int32_t* cu, int batch, int64_t row_elems,
                              void* out, void* stream);
 

@@ -41,6 +41,8 @@ __all__ = [
     "make_paged",
     "PrologueInputs",
     "make_prologue",
+    "GatedDeltaInputs",
+    "make_gated_delta",
     "WORKLOAD_NAMES",
 ]
 
@@ -378,3 +380,44 @@ def make_prologue(lengths, num_heads_q=32, num_heads_kv=8, head_dim=128, theta=1
     return PrologueInputs(lengths=lens, q=q, k=k, q_weight=np.ascontiguousarray(w[0]),
                           k_weight=np.ascontiguousarray(w[1]), cos=np.cos(ang).astype(np.float32),
                           sin=np.sin(ang).astype(np.float32), eps=float(eps))
+
+
+@dataclass
+class GatedDeltaInputs:
+    """Inputs of the varlen gated delta rule (linear attention) forward."""
+    lengths: np.ndarray                          # int64 [B]
+    q: np.ndarray = field(repr=False)            # bf16 values in fp32 [T, Hqk, Dk]
+    k: np.ndarray = field(repr=False)            # bf16 values in fp32 [T, Hqk, Dk]
+    v: np.ndarray = field(repr=False)            # bf16 values in fp32 [T, Hv, Dv]
+    g: np.ndarray = field(repr=False)            # fp32 [T, Hv], log decay <= 0
+    beta: np.ndarray = field(repr=False)         # fp32 [T, Hv], in (0, 1)
+    scale: float = 1.0
+
+    @property
+    def cu_seqlens(self) -> np.ndarray:
+        return np.concatenate([[0], np.cumsum(self.lengths)]).astype(np.int32)
+
+
+def make_gated_delta(lengths, num_heads_qk=16, num_heads_v=32, head_dim_k=128, head_dim_v=128,
+                     seed=0) -> GatedDeltaInputs:
+    """Seeded inputs shaped like a hybrid model's linear-attention layers.
+
+    q and k are N(0, 1) rows scaled to unit length per head (the layers
+    normalise q and k before the operator), then rounded to bf16; v is
+    N(0, 1) rounded to bf16; the decay exp(g) is uniform in [0.5, 1) and
+    beta = sigmoid(N(0, 1)), both stored fp32. scale = 1/sqrt(Dk).
+    """
+    lens = np.asarray(lengths, dtype=np.int64).reshape(-1)
+    t = int(lens.sum())
+    sq, sk, sv, sgb = np.random.SeedSequence(seed).spawn(4)
+    q = _normal(sq, (t, num_heads_qk, head_dim_k)).astype(np.float64)
+    k = _normal(sk, (t, num_heads_qk, head_dim_k)).astype(np.float64)
+    q /= np.maximum(np.linalg.norm(q, axis=-1, keepdims=True), 1e-30)
+    k /= np.maximum(np.linalg.norm(k, axis=-1, keepdims=True), 1e-30)
+    rng = np.random.default_rng(sgb)
+    g = np.log(rng.uniform(0.5, 1.0, (t, num_heads_v))).astype(np.float32)
+    beta = (1.0 / (1.0 + np.exp(-rng.standard_normal((t, num_heads_v))))).astype(np.float32)
+    return GatedDeltaInputs(lengths=lens, q=round_to_bf16(q.astype(np.float32), inplace=True),
+                            k=round_to_bf16(k.astype(np.float32), inplace=True),
+                            v=round_to_bf16(_normal(sv, (t, num_heads_v, head_dim_v)), inplace=True),
+                            g=g, beta=beta, scale=1.0 / math.sqrt(head_dim_k))
