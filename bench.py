@@ -211,7 +211,7 @@ def gated_delta_case(vfa, torch, lengths, reps=5, warmup=1):
     out = torch.empty((int(p.lengths.sum()), 32, 128), dtype=torch.bfloat16, device="cuda")
 
     def call():
-        vfa.gated_delta_rule_fwd(q, k, v, g, beta, cu, scale=p.scale, out=out)
+        vfa.gated_delta_rule_fwd(q, k, v, g, beta, cu, int(p.lengths.max()), scale=p.scale, out=out)
 
     ms = time_calls(call, reps, warmup, torch)
     t = median(ms)

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define VFA_ABI_VERSION 5
+#define VFA_ABI_VERSION 6
 
 typedef enum vfa_status {
   VFA_OK = 0,
@@ -293,21 +293,36 @@ int32_t qk_norm_rope(const void* q_in, const void* k_in, int32_t dtype,
  * g, beta       [total_tokens, num_heads_v]                fp32
  * cu_seqlens    device int32 [batch + 1], as for varlen_attn_fwd (caller
  *               contract; checked on the device under VFA_DEBUG)
+ * max_seqlen    host upper bound of every sequence's length (caller
+ *               contract, checked under VFA_DEBUG). It selects the path:
+ *               up to 16, a token-by-token fp32 recurrence that needs no
+ *               workspace; above, the chunked form (64-token chunks, two
+ *               kernels) whose per-chunk matrices go to the workspace.
  * initial_state [batch, num_heads_v, head_dim_k, head_dim_v] fp32, or NULL
  * out           [total_tokens, num_heads_v, head_dim_v]    bf16
  * final_state   [batch, num_heads_v, head_dim_k, head_dim_v] fp32, or NULL
- * The state is kept and updated in fp32; out is rounded once to bf16.
+ * workspace     device memory of at least
+ *               gated_delta_rule_fwd_workspace_size(total_tokens,
+ *               num_heads_v, max_seqlen) bytes, 16-byte aligned, owned by
+ *               the caller; its contents need no initialisation and are
+ *               overwritten. NULL with 0 bytes when the size query returns 0.
+ * Both paths keep the state in fp32 and round out once to bf16.
  * Supported: dtype VFA_BF16; head_dim_k and head_dim_v in {64, 128};
  * num_heads_v a multiple of num_heads_qk; scale finite.
- * batch == 0 returns VFA_OK.
+ * q, k, v, g, beta and out may be NULL when total_tokens == 0; the final
+ * state (the initial state, or zeros) is still written.
+ * Errors: VFA_ERR_WORKSPACE if the workspace is NULL or smaller than the
+ * query (nothing is launched). batch == 0 returns VFA_OK.
  */
+int64_t gated_delta_rule_fwd_workspace_size(int32_t total_tokens, int32_t num_heads_v, int32_t max_seqlen);
+
 int32_t gated_delta_rule_fwd(const void* q, const void* k, const void* v, int32_t dtype,
                              const float* g, const float* beta, const int32_t* cu_seqlens,
-                             int32_t batch, int32_t total_tokens,
+                             int32_t batch, int32_t total_tokens, int32_t max_seqlen,
                              int32_t num_heads_qk, int32_t num_heads_v,
                              int32_t head_dim_k, int32_t head_dim_v, float scale,
                              const float* initial_state, void* out, float* final_state,
-                             void* stream);
+                             void* workspace, int64_t workspace_bytes, void* stream);
 
 /* Last-token gather ([P1] core optimisation 1, embed(): x[cu_seqlens[1:] - 1]).
  *

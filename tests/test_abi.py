@@ -44,7 +44,7 @@ def test_exports_match_header(lib):
 
 
 def test_abi_version(lib):
-    assert lib.vfa_abi_version() == vfa._header_abi_version() == 5
+    assert lib.vfa_abi_version() == vfa._header_abi_version() == 6
 
 
 def test_status_strings(lib):
@@ -267,12 +267,13 @@ def test_qk_norm_rope_validation(lib, kw, code):
 
 
 def _gdn(lib, **kw):
-    a = dict(q=P, k=P, v=P, dtype=BF16, g=P, beta=P, cu=P, batch=2, t=16, hqk=16, hv=32, dk=128, dv=128,
-             scale=0.088, s0=None, out=P, s1=None, stream=None)
+    # max_seqlen 8 takes the token-by-token path, which needs no workspace.
+    a = dict(q=P, k=P, v=P, dtype=BF16, g=P, beta=P, cu=P, batch=2, t=16, ms=8, hqk=16, hv=32, dk=128, dv=128,
+             scale=0.088, s0=None, out=P, s1=None, ws=None, wsb=0, stream=None)
     a.update(kw)
     return lib.gated_delta_rule_fwd(a["q"], a["k"], a["v"], a["dtype"], a["g"], a["beta"], a["cu"], a["batch"],
-                                    a["t"], a["hqk"], a["hv"], a["dk"], a["dv"], a["scale"], a["s0"], a["out"],
-                                    a["s1"], a["stream"])
+                                    a["t"], a["ms"], a["hqk"], a["hv"], a["dk"], a["dv"], a["scale"], a["s0"],
+                                    a["out"], a["s1"], a["ws"], a["wsb"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -288,6 +289,20 @@ def _gdn(lib, **kw):
     (dict(dk=96), UNSUP),
     (dict(dv=32), UNSUP),
     (dict(scale=float("inf")), UNSUP),
+    (dict(ms=-1), SHAPE),
+    (dict(ms=100), WS),                              # chunked path without a workspace
+    (dict(ms=100, ws=P, wsb=16 * 32 * 520 - 1), WS),
+    (dict(ms=100, ws=P, wsb=16 * 32 * 520, dv=32), UNSUP),
 ])
 def test_gated_delta_validation(lib, kw, code):
     assert _gdn(lib, **kw) == code
+
+
+def test_gated_delta_workspace_size(lib):
+    """Lengths up to 16 take the recurrence (no workspace); above, the chunked form keeps two 64-wide
+    bf16 hi / lo rows (T and M) and two fp32 decay factors per (token, value head): 520 bytes."""
+    ws = lib.gated_delta_rule_fwd_workspace_size
+    assert ws(35324, 32, 16) == 0
+    assert ws(35324, 32, 17) == 35324 * 32 * 520
+    assert ws(0, 32, 8192) == 0
+    assert ws(1, 1, 8192) == 520

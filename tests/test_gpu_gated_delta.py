@@ -1,5 +1,8 @@
 """GPU parity: gated_delta_rule_fwd (varlen gated delta rule, fp32 state) against the fp64 oracle.
 
+Both paths are covered: max_seqlen up to 16 runs the token-by-token recurrence, above it the chunked form
+(64-token chunks; T = (I + A)^-1 and M per chunk, bf16 hi / lo products on MFMA).
+
 Tolerances: out is one bf16 rounding of an fp32 result, |out - ref| <= 2^-7 |ref| + 1e-4; the fp32 final
 state, |S - ref| <= 1e-4 + 1e-4 |ref| (fp32 arithmetic over the sequence against fp64 on the same
 bf16-exact inputs)."""
@@ -33,27 +36,34 @@ def check_close(name, got, ref, rtol, atol):
 
 
 CASES = {
-    # name: (lengths, Hqk, Hv, Dk, Dv, with initial state)
-    "d128_gva": ([1, 17, 64, 200, 33, 0], 2, 4, 128, 128, False),
-    "d64_mh": ([40, 3, 130], 3, 3, 64, 64, True),
-    "dk128_dv64": ([70, 129], 1, 2, 128, 64, True),
-    "dk64_dv128": ([31, 96, 5], 2, 2, 64, 128, False),
+    # name: (lengths, Hqk, Hv, Dk, Dv, with initial state, max_seqlen or None for max(lengths))
+    "d128_gva": ([1, 17, 64, 200, 33, 0], 2, 4, 128, 128, False, None),
+    "d64_mh": ([40, 3, 130], 3, 3, 64, 64, True, None),
+    "dk128_dv64": ([70, 129], 1, 2, 128, 64, True, None),
+    "dk64_dv128": ([31, 96, 5], 2, 2, 64, 128, False, None),
+    "chunk_edges": ([63, 64, 65, 127, 128, 129, 1, 191], 1, 2, 128, 128, True, None),
+    "recurrent_short": ([1, 16, 5, 0, 9, 16], 2, 4, 128, 128, True, None),
+    "recurrent_d64": ([7, 12, 3], 1, 1, 64, 64, False, None),
+    "chunked_loose_bound": ([1, 16, 5, 0, 9, 16], 2, 4, 128, 128, True, 300),
+    "all_empty": ([0, 0, 0], 1, 2, 64, 128, True, None),
 }
 
 
 @pytest.mark.parametrize("name", sorted(CASES))
 def test_gated_delta_parity(name):
     torch = need_gpu()
-    lens, hqk, hv, dk, dv, with_init = CASES[name]
+    lens, hqk, hv, dk, dv, with_init, bound = CASES[name]
     p = make_gated_delta(lens, hqk, hv, dk, dv, seed=len(name))
-    print(f"[case] gated_delta {name}: lengths={lens} Hqk={hqk} Hv={hv} Dk={dk} Dv={dv} init={with_init}", flush=True)
+    ms = max(lens) if bound is None else bound
+    print(f"[case] gated_delta {name}: lengths={lens} Hqk={hqk} Hv={hv} Dk={dk} Dv={dv} init={with_init} "
+          f"max_seqlen={ms}", flush=True)
     x = dev_inputs(p)
     s0 = None
     s0_dev = None
     if with_init:
         s0 = np.random.default_rng(7).standard_normal((len(lens), hv, dk, dv)).astype(np.float32) * 0.5
         s0_dev = torch.from_numpy(s0).cuda()
-    out, fin = vfa.gated_delta_rule_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["cu"], scale=p.scale,
+    out, fin = vfa.gated_delta_rule_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["cu"], ms, scale=p.scale,
                                         initial_state=s0_dev, output_final_state=True)
     torch.cuda.synchronize()
     o_ref, f_ref = oracle.gated_delta_rule(p.q, p.k, p.v, p.g, p.beta, p.cu_seqlens, p.scale, initial_state=s0)
@@ -61,32 +71,69 @@ def test_gated_delta_parity(name):
     check_close(f"{name}_state", host64(fin), f_ref, 1e-4, 1e-4)
 
 
-def test_gated_delta_continuation_is_exact():
-    """Two calls, the second starting from the first's final state, give bit for bit the outputs and
-    state of one call over the whole sequences (the kernel keeps the state in fp32 between tokens)."""
+def _continuation(lengths, split, seed):
+    """Runs the packed sequences whole, then as two calls (the first `split[b]` tokens of each sequence,
+    then the rest from the first call's final state); returns both outputs and final states."""
     torch = need_gpu()
-    a = make_gated_delta([100, 37], 2, 4, 128, 128, seed=91)
-    print("[case] gated_delta continuation", flush=True)
+    a = make_gated_delta(lengths, 2, 4, 128, 128, seed=seed)
     x = dev_inputs(a)
-    whole, fin = vfa.gated_delta_rule_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["cu"], scale=a.scale,
-                                          output_final_state=True)
-    cu1 = np.array([0, 60, 60 + 20], dtype=np.int32)            # first 60 and 20 tokens of each sequence
-    idx1 = np.r_[0:60, 100:120]
-    idx2 = np.r_[60:100, 120:137]
-    cu2 = np.array([0, 40, 57], dtype=np.int32)
+    whole, fin = vfa.gated_delta_rule_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["cu"], max(lengths),
+                                          scale=a.scale, output_final_state=True)
+    starts = np.r_[0, np.cumsum(lengths)[:-1]]
+    idx1 = np.concatenate([np.arange(s0, s0 + m) for s0, m in zip(starts, split)])
+    idx2 = np.concatenate([np.arange(s0 + m, s0 + n) for s0, m, n in zip(starts, split, lengths)])
+    rest = [n - m for n, m in zip(lengths, split)]
 
-    def part(idx, cu, init):
+    def part(idx, lens, init):
         ii = torch.from_numpy(idx).cuda()
+        cu = torch.from_numpy(np.r_[0, np.cumsum(lens)].astype(np.int32)).cuda()
         return vfa.gated_delta_rule_fwd(x["q"][ii].contiguous(), x["k"][ii].contiguous(), x["v"][ii].contiguous(),
-                                        x["g"][ii].contiguous(), x["beta"][ii].contiguous(),
-                                        torch.from_numpy(cu).cuda(), scale=a.scale, initial_state=init,
-                                        output_final_state=True)
-    o1, f1 = part(idx1, cu1, None)
-    o2, f2 = part(idx2, cu2, f1)
+                                        x["g"][ii].contiguous(), x["beta"][ii].contiguous(), cu, max(lens),
+                                        scale=a.scale, initial_state=init, output_final_state=True)
+    o1, f1 = part(idx1, split, None)
+    o2, f2 = part(idx2, rest, f1)
     torch.cuda.synchronize()
-    assert torch.equal(o1, whole[torch.from_numpy(idx1).cuda()])
-    assert torch.equal(o2, whole[torch.from_numpy(idx2).cuda()])
-    assert torch.equal(f2, fin)
+    return (whole[torch.from_numpy(idx1).cuda()], o1), (whole[torch.from_numpy(idx2).cuda()], o2), (fin, f2)
+
+
+def test_gated_delta_continuation_is_exact_chunked():
+    """Split at 64-token chunk boundaries, two chunked calls (the second from the first's fp32 final
+    state) repeat one whole call's chunks exactly: outputs and state bit for bit."""
+    torch = need_gpu()
+    print("[case] gated_delta continuation, chunked", flush=True)
+    for want, got in _continuation([100, 137], [64, 128], seed=91):
+        assert torch.equal(got, want)
+
+
+def test_gated_delta_continuation_is_exact_recurrent():
+    """The token-by-token path (lengths up to 16) keeps the state in fp32 between tokens, so a split
+    anywhere gives the whole call's outputs and state bit for bit."""
+    torch = need_gpu()
+    print("[case] gated_delta continuation, recurrent", flush=True)
+    for want, got in _continuation([10, 15, 7], [4, 9, 1], seed=92):
+        assert torch.equal(got, want)
+
+
+def test_gated_delta_paths_agree():
+    """The same short sequences through both paths (max_seqlen 16, then a loose bound of 17): each is
+    within the oracle bound, so they differ by at most the sum of the two bounds."""
+    torch = need_gpu()
+    lens = [16, 3, 11, 1]
+    p = make_gated_delta(lens, 2, 4, 128, 128, seed=94)
+    print("[case] gated_delta paths agree", flush=True)
+    x = dev_inputs(p)
+    outs = [vfa.gated_delta_rule_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["cu"], ms, scale=p.scale,
+                                     output_final_state=True) for ms in (16, 17)]
+    torch.cuda.synchronize()
+    (o_r, f_r), (o_c, f_c) = ((host64(o), host64(f)) for o, f in outs)
+    ref_o, ref_f = oracle.gated_delta_rule(p.q, p.k, p.v, p.g, p.beta, p.cu_seqlens, p.scale)
+    # |o_r| is within 2^-7 of |ref|, so two oracle bounds fit inside 2.1 * 2^-7 |o_r| + 2e-4.
+    check_close("paths_out", o_c, o_r, 2.1 * 2.0 ** -7, 2e-4)
+    check_close("paths_state", f_c, f_r, 2.1e-4, 2e-4)
+    check_close("recurrent_vs_oracle", o_r, ref_o, 2.0 ** -7, 1e-4)
+    check_close("chunked_vs_oracle", o_c, ref_o, 2.0 ** -7, 1e-4)
+    check_close("recurrent_state_vs_oracle", f_r, ref_f, 1e-4, 1e-4)
+    check_close("chunked_state_vs_oracle", f_c, ref_f, 1e-4, 1e-4)
 
 
 def test_gated_delta_long_prefill_shape_sampled():
@@ -97,8 +144,8 @@ def test_gated_delta_long_prefill_shape_sampled():
     p = make_gated_delta(lens, 16, 32, 128, 128, seed=92)
     print(f"[case] gated_delta long-prefill shape T={int(lens.sum())}", flush=True)
     x = dev_inputs(p)
-    out, fin = vfa.gated_delta_rule_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["cu"], scale=p.scale,
-                                        output_final_state=True)
+    out, fin = vfa.gated_delta_rule_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["cu"], int(lens.max()),
+                                        scale=p.scale, output_final_state=True)
     torch.cuda.synchronize()
     cu = p.cu_seqlens
     longest = int(np.argmax(lens))

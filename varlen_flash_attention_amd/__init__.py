@@ -19,8 +19,9 @@ Entry points (same names as the C ABI in include/vfa.h):
                     max_seqlen_k, softmax_scale=None, causal=True, out_dtype=None) -> (out, lse)
   paged_attn_decode_workspace_size(...) -> bytes
   qk_norm_rope(q, k, q_weight, k_weight, cos, sin, eps=1e-6, q_out=None, k_out=None) -> (q_out, k_out)
-  gated_delta_rule_fwd(q, k, v, g, beta, cu_seqlens, scale=None, initial_state=None,
-                       output_final_state=False) -> (out, final_state or None)
+  gated_delta_rule_fwd(q, k, v, g, beta, cu_seqlens, max_seqlen, scale=None, initial_state=None,
+                       output_final_state=False, out=None) -> (out, final_state or None)
+  gated_delta_rule_fwd_workspace_size(total_tokens, num_heads_v, max_seqlen) -> bytes
 """
 from __future__ import annotations
 
@@ -43,6 +44,7 @@ __all__ = [
     "paged_attn_decode_workspace_size",
     "qk_norm_rope",
     "gated_delta_rule_fwd",
+    "gated_delta_rule_fwd_workspace_size",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -133,7 +135,10 @@ def load_library() -> ctypes.CDLL:
     lib.gated_delta_rule_fwd.restype = c.c_int32
     lib.gated_delta_rule_fwd.argtypes = [c.c_void_p, c.c_void_p, c.c_void_p, c.c_int32, c.c_void_p, c.c_void_p,
                                          c.c_void_p, c.c_int32, c.c_int32, c.c_int32, c.c_int32, c.c_int32,
-                                         c.c_int32, c.c_float, c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p]
+                                         c.c_int32, c.c_int32, c.c_float, c.c_void_p, c.c_void_p, c.c_void_p,
+                                         c.c_void_p, c.c_int64, c.c_void_p]
+    lib.gated_delta_rule_fwd_workspace_size.restype = c.c_int64
+    lib.gated_delta_rule_fwd_workspace_size.argtypes = [c.c_int32, c.c_int32, c.c_int32]
     got, want = lib.vfa_abi_version(), _header_abi_version()
     if got != want:
         raise RuntimeError(f"{path} has ABI version {got}, include/vfa.h expects {want}: stale library")
@@ -401,11 +406,17 @@ def qk_norm_rope(q, k, q_weight, k_weight, cos, sin, eps: float = 1e-6, q_out=No
     return q_out, k_out
 
 
-def gated_delta_rule_fwd(q, k, v, g, beta, cu_seqlens, scale: float | None = None, initial_state=None,
-                         output_final_state: bool = False, out=None):
+def gated_delta_rule_fwd_workspace_size(total_tokens: int, num_heads_v: int, max_seqlen: int) -> int:
+    return int(load_library().gated_delta_rule_fwd_workspace_size(int(total_tokens), int(num_heads_v),
+                                                                  int(max_seqlen)))
+
+
+def gated_delta_rule_fwd(q, k, v, g, beta, cu_seqlens, max_seqlen: int, scale: float | None = None,
+                         initial_state=None, output_final_state: bool = False, out=None):
     """Varlen gated delta rule forward. q, k [T, Hqk, Dk] and v [T, Hv, Dv] bf16; g, beta [T, Hv] fp32;
-    cu_seqlens int32 [B+1]; initial_state [B, Hv, Dk, Dv] fp32 or None. Default scale 1/sqrt(Dk).
-    Returns (out [T, Hv, Dv] bf16, final_state [B, Hv, Dk, Dv] fp32 or None)."""
+    cu_seqlens int32 [B+1] on the GPU; max_seqlen a host upper bound of the lengths (it also picks the
+    token-by-token path up to 16 and the chunked one above); initial_state [B, Hv, Dk, Dv] fp32 or None.
+    Default scale 1/sqrt(Dk). Returns (out [T, Hv, Dv] bf16, final_state [B, Hv, Dk, Dv] fp32 or None)."""
     torch = _torch()
     lib = load_library()
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -435,10 +446,14 @@ def gated_delta_rule_fwd(q, k, v, g, beta, cu_seqlens, scale: float | None = Non
     _check_gpu("out", out, 3)
     final = torch.empty((batch, hv, dk, dv), dtype=torch.float32, device=q.device) if output_final_state else None
     sc = 1.0 / math.sqrt(dk) if scale is None else float(scale)
+    ws_bytes = gated_delta_rule_fwd_workspace_size(tt, hv, max_seqlen)
+    workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes > 0 else None
     st = lib.gated_delta_rule_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), VFA_BF16, g.data_ptr(), beta.data_ptr(),
-                                  cu_seqlens.data_ptr(), batch, tt, hqk, hv, dk, dv, sc,
+                                  cu_seqlens.data_ptr(), batch, tt, int(max_seqlen), hqk, hv, dk, dv, sc,
                                   initial_state.data_ptr() if initial_state is not None else None, out.data_ptr(),
-                                  final.data_ptr() if final is not None else None, _stream_ptr(q.device))
+                                  final.data_ptr() if final is not None else None,
+                                  workspace.data_ptr() if workspace is not None else None, ws_bytes,
+                                  _stream_ptr(q.device))
     if st != 0:
         raise VfaError(st, "gated_delta_rule_fwd")
     return out, final

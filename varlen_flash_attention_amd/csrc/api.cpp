@@ -296,21 +296,35 @@ VFA_API int32_t qk_norm_rope(const void* q_in, const void* k_in, int32_t dtype, 
   return vfa::launch_qk_norm_rope(a) == 0 ? VFA_OK : VFA_ERR_LAUNCH;
 }
 
+// Sequences up to this length take the token-by-token recurrence (one
+// kernel, no workspace); longer ones the chunked form.
+constexpr int kGdnRecurrentMaxLen = 16;
+
+VFA_API int64_t gated_delta_rule_fwd_workspace_size(int32_t total_tokens, int32_t num_heads_v, int32_t max_seqlen) {
+  if (total_tokens <= 0 || num_heads_v <= 0 || max_seqlen <= kGdnRecurrentMaxLen) return 0;
+  return (int64_t)vfa::gated_delta_chunk_workspace(total_tokens, num_heads_v);
+}
+
 VFA_API int32_t gated_delta_rule_fwd(const void* q, const void* k, const void* v, int32_t dtype, const float* g,
                                      const float* beta, const int32_t* cu_seqlens, int32_t batch,
-                                     int32_t total_tokens, int32_t num_heads_qk, int32_t num_heads_v,
-                                     int32_t head_dim_k, int32_t head_dim_v, float scale,
-                                     const float* initial_state, void* out, float* final_state, void* stream) {
-  if (batch < 0 || total_tokens < 0 || num_heads_qk <= 0 || num_heads_v <= 0) return VFA_ERR_SHAPE;
+                                     int32_t total_tokens, int32_t max_seqlen, int32_t num_heads_qk,
+                                     int32_t num_heads_v, int32_t head_dim_k, int32_t head_dim_v, float scale,
+                                     const float* initial_state, void* out, float* final_state, void* workspace,
+                                     int64_t workspace_bytes, void* stream) {
+  if (batch < 0 || total_tokens < 0 || max_seqlen < 0 || num_heads_qk <= 0 || num_heads_v <= 0)
+    return VFA_ERR_SHAPE;
   if (num_heads_v % num_heads_qk != 0) return VFA_ERR_SHAPE;
   if (batch == 0) return VFA_OK;
-  if (!q || !k || !v || !g || !beta || !cu_seqlens || !out) return VFA_ERR_NULL;
+  // With no tokens the token tensors may be NULL; the final state is still written.
+  if (!cu_seqlens || (total_tokens > 0 && (!q || !k || !v || !g || !beta || !out))) return VFA_ERR_NULL;
   if (dtype != VFA_BF16) return VFA_ERR_UNSUPPORTED;
   if (head_dim_k != 64 && head_dim_k != 128) return VFA_ERR_UNSUPPORTED;
   if (head_dim_v != 64 && head_dim_v != 128) return VFA_ERR_UNSUPPORTED;
   if (!std::isfinite(scale)) return VFA_ERR_UNSUPPORTED;
+  const int64_t need = gated_delta_rule_fwd_workspace_size(total_tokens, num_heads_v, max_seqlen);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return VFA_ERR_WORKSPACE;
   if (debug_checks()) {
-    const int r = vfa::check_cu_seqlens(cu_seqlens, total_tokens, 0x7fffffff, nullptr, 0, 0, batch, stream);
+    const int r = vfa::check_cu_seqlens(cu_seqlens, total_tokens, max_seqlen, nullptr, 0, 0, batch, stream);
     if (r < 0) return VFA_ERR_LAUNCH;
     if (r > 0) return VFA_ERR_SHAPE;
   }
@@ -319,5 +333,6 @@ VFA_API int32_t gated_delta_rule_fwd(const void* q, const void* k, const void* v
   a.batch = batch; a.tokens = total_tokens; a.hqk = num_heads_qk; a.hv = num_heads_v;
   a.dk = head_dim_k; a.dv = head_dim_v; a.scale = scale;
   a.s_init = initial_state; a.out = out; a.s_final = final_state; a.stream = stream;
-  return vfa::launch_gated_delta(a) == 0 ? VFA_OK : VFA_ERR_LAUNCH;
+  const int rc = need > 0 ? vfa::launch_gated_delta_chunked(a, max_seqlen, workspace) : vfa::launch_gated_delta(a);
+  return rc == 0 ? VFA_OK : VFA_ERR_LAUNCH;
 }

@@ -111,6 +111,10 @@ int launch_attn_update(const float* lse, const void* go, int go_dtype, int sp, i
                        int update_type, void* out, float* lse_out, void* stream);
 int launch_qk_norm_rope(const QkNormRopeArgs& a);
 int launch_gated_delta(const GatedDeltaArgs& a);
+// Chunked form (gated_delta_chunk.hip): bytes of workspace for `tokens` packed
+// tokens and hv value heads, and the two-kernel launch using it.
+size_t gated_delta_chunk_workspace(long long tokens, int hv);
+int launch_gated_delta_chunked(const GatedDeltaArgs& a, int max_seqlen, void* workspace);
 int launch_last_token_gather(const void* x, int esize, const int32_t* cu, int batch, int64_t row_elems,
                              void* out, void* stream);
 
