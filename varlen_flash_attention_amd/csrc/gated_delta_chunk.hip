@@ -17,22 +17,22 @@
 //                    T = (I + A)^-1 by forward substitution in fp32, then T and
 //                    M as bf16 hi / lo pairs and the two decay factors per token
 //                    into the workspace.
-//   gdn_chunk_kernel one workgroup per (sequence, value head), one wave per 32
+//   gdn_chunk_kernel one workgroup per (sequence, value head), one wave per 16
 //                    state columns, chunks in order: y = K S and Q S, then
 //                    U = T r with r = beta (V - e^gamma y), then M U for the
 //                    output and K^T U~ for the state.
 //
-// Precision: the state stays fp32 in MFMA accumulators. Every product with an
-// fp32 operand splits it into bf16 hi + lo and takes hi.hi + hi.lo + lo.hi (K
-// and Q are bf16 already, so their products take two passes); the dropped lo.lo
-// term is below 2^-16 relative.
+// Precision: the state stays fp32 in MFMA accumulators. Products with an fp32
+// operand split it into bf16 hi + lo and take hi.hi + hi.lo + lo.hi (K and Q
+// are bf16 already, so their products take hi and lo of the other side); the
+// dropped lo.lo term is below 2^-16 relative. (Taking S's hi part alone in
+// y = K S leaves the output within its bound, but a nonzero initial state then
+// drifts past the state's bound, so the lo pass stays.)
 //
-// Operand layout (v_mfma_f32_32x32x16_bf16): lane (l32, half) holds 8 values of
-// k for its row / column. An accumulator's registers 8s .. 8s+7 hold rows
-// 16s + {4 half + 0..3, 8 + 4 half + 0..3}, so accumulators feed the next
-// product as B operands directly when the memory-side A operand reads its k
-// values in that order (two 8-byte runs). K^T comes from the staged K chunk
-// through the LDS transpose read, which delivers the same order.
+// Operand layout: accumulators feed the next product as B operands directly
+// when the memory-side A operand reads its k values in the accumulator's row
+// order; K^T and V come from the staged chunk through the LDS transpose read,
+// which delivers that order.
 #include "common.h"
 #include "launch.h"
 
@@ -45,31 +45,10 @@ __device__ __forceinline__ bf16x8 join(bf16x4 a, bf16x4 b) {
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// The two 8-byte runs {4 half + 0..3} and {8 + 4 half + 0..3} of a 16-value k
-// step starting at p (bf16 elements; p already offset by 4 * half).
-__device__ __forceinline__ bf16x8 load_perm(const bf16* p) {
-  return join(*(const bf16x4*)p, *(const bf16x4*)(p + 8));
-}
-
-__device__ __forceinline__ bf16x8 lds_perm(const char VFA_LDS* p) {
-  return join(*(const bf16x4 VFA_LDS*)p, *(const bf16x4 VFA_LDS*)(p + 16));
-}
-
 __device__ __forceinline__ bf16x8 lds_read_tr(const char VFA_LDS* p0, const char VFA_LDS* p1) {
   i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 VFA_LDS*)p0);
   i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 VFA_LDS*)p1);
   return join(__builtin_bit_cast(bf16x4, lo), __builtin_bit_cast(bf16x4, hi));
-}
-
-// bf16 hi / lo split of 8 consecutive accumulator registers: x = hi + lo + O(2^-17 |x|).
-__device__ __forceinline__ void split8(const f32x16& acc, int base, bf16x8& hi, bf16x8& lo) {
-#pragma unroll
-  for (int y = 0; y < 8; y += 2) {
-    const bf16x2 h = f32x2_to_bf16x2(acc[base + y], acc[base + y + 1]);
-    const bf16x2 l = f32x2_to_bf16x2(acc[base + y] - (float)h[0], acc[base + y + 1] - (float)h[1]);
-    hi[y] = h[0]; hi[y + 1] = h[1];
-    lo[y] = l[0]; lo[y + 1] = l[1];
-  }
 }
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -215,18 +194,28 @@ __global__ __launch_bounds__(64) void gdn_prep_kernel(const bf16* __restrict__ q
 
 // ---------------------------------------------------------------------------
 // Phase 2: per (sequence, value head), chunks in order; wave w owns state
-// columns 32 w .. 32 w + 31. Each chunk's K, Q, T, M and V rows (and the
-// per-token beta and decay factors) are loaded into registers one chunk ahead
-// and stored to LDS after the barrier, so the chunk's chain of products reads
-// only LDS and waits on global memory once per chunk at most.
+// columns 16 w .. 16 w + 15 (v_mfma_f32_16x16x32_bf16: lane (c16, g) holds
+// k-slots 8 g + 0..7 of its row or column, and accumulator rows 4 g + 0..3).
+// Two 16-row accumulator tiles form one 32-deep B operand, k-slot 8 g + x
+// holding row {4 g + x, 16 + 4 g + x - 4}; memory-side A operands read their
+// k values in that order (two 8-byte runs 32 bytes apart), and the transposed
+// LDS read pair 16 rows apart delivers it too. Each chunk's K, Q, T, M and V
+// rows (and the per-token beta and decay factors) are loaded into registers
+// one chunk ahead and stored to LDS after the barrier, so the chunk's chain of
+// products reads only LDS.
 template <int DK, int WAVES>
 struct ChunkSmem {
   static constexpr int THREADS = WAVES * 64;
-  static constexpr int DV = WAVES * 32;
-  static constexpr int KSTR = DK * 2 + 64;     // K rows: transposed reads conflict-free
+  static constexpr int DV = WAVES * 16;
+  // Row strides of 2 D + 16 bytes (D = 64 or 128): both the A-operand row
+  // reads (lane (c16, g) at row c16, dword 2 g) and the transposed reads (rows
+  // 4 g + 0..3, dwords 2 (i & 3)) then touch each of the 64 banks exactly
+  // twice per wave, the minimum for 8-byte accesses (a 64-byte pad folds
+  // them four ways).
+  static constexpr int KSTR = DK * 2 + 16;     // K rows (row and transposed reads)
   static constexpr int QSTR = DK * 2 + 16;     // Q rows
   static constexpr int TSTR = 2 * kC * 2 + 16; // T and M rows (hi | lo)
-  static constexpr int VSTR = DV * 2 + 64;     // V rows: transposed reads
+  static constexpr int VSTR = DV * 2 + 16;     // V rows (transposed reads)
   static constexpr int K_OFF = 0;
   static constexpr int Q_OFF = K_OFF + kC * KSTR;
   static constexpr int T_OFF = Q_OFF + kC * QSTR;
@@ -241,6 +230,27 @@ struct ChunkSmem {
                 "pieces must split evenly over the workgroup");
 };
 
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// A operand read for the 16x16x32 k order: runs at p and p + 32 bytes.
+__device__ __forceinline__ bf16x8 lds_perm16(const char VFA_LDS* p) {
+  return join(*(const bf16x4 VFA_LDS*)p, *(const bf16x4 VFA_LDS*)(p + 32));
+}
+
+// bf16 hi / lo of two 16-row accumulator tiles as one 32-deep B operand.
+__device__ __forceinline__ void split_pair(const f32x4& t0, const f32x4& t1, bf16x8& hi, bf16x8& lo) {
+  const float x[8] = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
+#pragma unroll
+  for (int y = 0; y < 8; y += 2) {
+    const bf16x2 h = f32x2_to_bf16x2(x[y], x[y + 1]);
+    const bf16x2 l = f32x2_to_bf16x2(x[y] - (float)h[0], x[y + 1] - (float)h[1]);
+    hi[y] = h[0]; hi[y + 1] = h[1];
+    lo[y] = l[0]; lo[y + 1] = l[1];
+  }
+}
+
 template <int DK, int WAVES>
 __global__ __launch_bounds__(WAVES * 64) void gdn_chunk_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
@@ -249,7 +259,7 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_chunk_kernel(
     const bf16* __restrict__ wt, const bf16* __restrict__ wm, const float* __restrict__ we) {
   using S = ChunkSmem<DK, WAVES>;
   constexpr int DV = S::DV;
-  constexpr int NDT = DK / 32;          // 32-row tiles of the state
+  constexpr int NDT = DK / 16;          // 16-row tiles of the state
   __shared__ __attribute__((aligned(16))) char smem[S::BYTES];
   __shared__ __attribute__((aligned(16))) float se1[kC], se2[kC], sbt[kC];
   char VFA_LDS* lds = (char VFA_LDS*)smem;
@@ -265,24 +275,24 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_chunk_kernel(
   const int ts = cu[b];
   const int len = cu[b + 1] - ts;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, l32 = lane & 31, half = lane >> 5;
-  const int col0 = (tid >> 6) * 32;
-  const int col = col0 + l32;
+  const int lane = tid & 63, c16 = lane & 15, g = lane >> 4;
+  const int col0 = (tid >> 6) * 16;
+  const int col = col0 + c16;
 
-  // Transposed reads: lane (l32, half) receives column l32 of a 32-wide block
-  // for rows {4 half + 0..3} (first read) and {8 + 4 half + 0..3}.
-  const int tr_grp = lane >> 4, tr_i = lane & 15;
-  const int tr_key = (tr_grp >> 1) * 4 + (tr_i >> 2);
-  const int tr_d = (tr_grp & 1) * 16 + 4 * (tr_i & 3);
+  // Transposed reads: lane (c16, g) receives column c16 of a 16-wide block for
+  // rows {4 g + 0..3} (first read) and {16 + 4 g + 0..3} (second, 16 rows on).
+  const int tr_i = lane & 15;
+  const int tr_key = g * 4 + (tr_i >> 2);
+  const int tr_d = 4 * (tr_i & 3);
 
-  // State rows d = 32 dt + 8 (r >> 2) + 4 half + (r & 3), column col.
-  f32x16 st[NDT];
+  // State rows d = 16 dt + 4 g + r, column col.
+  f32x4 st[NDT];
   const size_t sbase = ((size_t)b * hv + h) * DK * DV + col;
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
-      st[dt][r] = s_init ? s_init[sbase + (size_t)(32 * dt + 8 * (r >> 2) + 4 * half + (r & 3)) * DV] : 0.f;
+    for (int r = 0; r < 4; ++r)
+      st[dt][r] = s_init ? s_init[sbase + (size_t)(16 * dt + 4 * g + r) * DV] : 0.f;
 
   // Chunk loads into registers. Rows past the chunk's end repeat its last row
   // (finite values): their beta and decay factors are zero, so they add nothing.
@@ -358,96 +368,93 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_chunk_kernel(
     __syncthreads();
     if (c0 + kC < len) load_chunk(c0 + kC);   // next chunk, in flight during this one
 
-    // S as B operands (hi / lo) for the 16-row k steps of the state.
-    bf16x8 sh[DK / 16], sl[DK / 16];
+    // S as B operands (32-deep k steps over the state rows), hi and lo.
+    bf16x8 sh[DK / 32], sl[DK / 32];
 #pragma unroll
-    for (int ks = 0; ks < DK / 16; ++ks) split8(st[ks >> 1], (ks & 1) * 8, sh[ks], sl[ks]);
+    for (int ks = 0; ks < DK / 32; ++ks) split_pair(st[2 * ks], st[2 * ks + 1], sh[ks], sl[ks]);
 
-    // y = K S (rows: chunk tokens) and Q S.
-    f32x16 y[2] = {}, qs[2] = {};
+    // y = K S and Q S (hi and lo); rows: chunk tokens 16 mt + 4 g + r.
+    f32x4 y[4] = {}, qs[4] = {};
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      const char VFA_LDS* kr = sk + (32 * mt + l32) * S::KSTR + 8 * half;
-      const char VFA_LDS* qr = sq + (32 * mt + l32) * S::QSTR + 8 * half;
+    for (int mt = 0; mt < 4; ++mt) {
+      const char VFA_LDS* kr = sk + (16 * mt + c16) * S::KSTR + 8 * g;
+      const char VFA_LDS* qr = sq + (16 * mt + c16) * S::QSTR + 8 * g;
 #pragma unroll
-      for (int ks = 0; ks < DK / 16; ++ks) {
-        const bf16x8 ak = lds_perm(kr + 32 * ks);
-        const bf16x8 aq = lds_perm(qr + 32 * ks);
-        y[mt] = mfma(ak, sh[ks], y[mt]);
-        y[mt] = mfma(ak, sl[ks], y[mt]);
-        qs[mt] = mfma(aq, sh[ks], qs[mt]);
-        qs[mt] = mfma(aq, sl[ks], qs[mt]);
+      for (int ks = 0; ks < DK / 32; ++ks) {
+        const bf16x8 ak = lds_perm16(kr + 64 * ks);
+        const bf16x8 aq = lds_perm16(qr + 64 * ks);
+        y[mt] = mfma16(ak, sh[ks], y[mt]);
+        y[mt] = mfma16(ak, sl[ks], y[mt]);
+        qs[mt] = mfma16(aq, sh[ks], qs[mt]);
+        qs[mt] = mfma16(aq, sl[ks], qs[mt]);
       }
     }
 
     // r = beta (v - e^gamma y) in place, and the e^gamma scaling of Q S. V
     // comes through the transposed read, already in accumulator row order.
 #pragma unroll
-    for (int s16 = 0; s16 < 4; ++s16) {
-      const char VFA_LDS* p = sv + (16 * s16 + tr_key) * S::VSTR + tr_d * 2 + 64 * (col0 / 32);
-      const bf16x8 vv = lds_read_tr(p, p + 8 * S::VSTR);
-      const int mt = s16 >> 1, rb = (s16 & 1) * 8;
+    for (int s32 = 0; s32 < 2; ++s32) {
+      const char VFA_LDS* p = sv + (32 * s32 + tr_key) * S::VSTR + tr_d * 2 + 2 * col0;
+      const bf16x8 vv = lds_read_tr(p, p + 16 * S::VSTR);
 #pragma unroll
-      for (int y4 = 0; y4 < 2; ++y4) {
-        const int i0 = 16 * s16 + 8 * y4 + 4 * half;
+      for (int hh = 0; hh < 2; ++hh) {
+        const int mt = 2 * s32 + hh;
+        const int i0 = 16 * mt + 4 * g;
         const f32x4 e1 = *(const f32x4*)&se1[i0];
         const f32x4 bt = *(const f32x4*)&sbt[i0];
 #pragma unroll
         for (int z = 0; z < 4; ++z) {
-          const int r = rb + 4 * y4 + z;
-          y[mt][r] = bt[z] * ((float)vv[4 * y4 + z] - e1[z] * y[mt][r]);
-          qs[mt][r] *= e1[z];
+          y[mt][z] = bt[z] * ((float)vv[4 * hh + z] - e1[z] * y[mt][z]);
+          qs[mt][z] *= e1[z];
         }
       }
     }
-    bf16x8 rh[4], rl[4];
+    bf16x8 rh[2], rl[2];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) split8(y[kk >> 1], (kk & 1) * 8, rh[kk], rl[kk]);
+    for (int kk = 0; kk < 2; ++kk) split_pair(y[2 * kk], y[2 * kk + 1], rh[kk], rl[kk]);
 
     // U = T r.
-    f32x16 u[2] = {};
+    f32x4 u[4] = {};
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      const char VFA_LDS* tr = stt + (32 * mt + l32) * S::TSTR + 8 * half;
+    for (int mt = 0; mt < 4; ++mt) {
+      const char VFA_LDS* tr = stt + (16 * mt + c16) * S::TSTR + 8 * g;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const bf16x8 th = lds_perm(tr + 32 * kk), tl = lds_perm(tr + 2 * kC + 32 * kk);
-        u[mt] = mfma(th, rh[kk], u[mt]);
-        u[mt] = mfma(th, rl[kk], u[mt]);
-        u[mt] = mfma(tl, rh[kk], u[mt]);
+      for (int kk = 0; kk < 2; ++kk) {
+        const bf16x8 th = lds_perm16(tr + 64 * kk), tl = lds_perm16(tr + 2 * kC + 64 * kk);
+        u[mt] = mfma16(th, rh[kk], u[mt]);
+        u[mt] = mfma16(th, rl[kk], u[mt]);
+        u[mt] = mfma16(tl, rh[kk], u[mt]);
       }
     }
 
     // U and U~ = e^(gamma_end - gamma) U as B operands.
-    bf16x8 uh[4], ul[4];
+    bf16x8 uh[2], ul[2];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) split8(u[kk >> 1], (kk & 1) * 8, uh[kk], ul[kk]);
+    for (int kk = 0; kk < 2; ++kk) split_pair(u[2 * kk], u[2 * kk + 1], uh[kk], ul[kk]);
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < 4; ++mt) {
+      const f32x4 e2 = *(const f32x4*)&se2[16 * mt + 4 * g];
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const f32x4 e2 = *(const f32x4*)&se2[32 * mt + 8 * g4 + 4 * half];
+      for (int z = 0; z < 4; ++z) u[mt][z] *= e2[z];
+    }
+    bf16x8 wh[2], wl[2];
 #pragma unroll
-        for (int z = 0; z < 4; ++z) u[mt][4 * g4 + z] *= e2[z];
-      }
-    bf16x8 wh[4], wl[4];
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) split8(u[kk >> 1], (kk & 1) * 8, wh[kk], wl[kk]);
+    for (int kk = 0; kk < 2; ++kk) split_pair(u[2 * kk], u[2 * kk + 1], wh[kk], wl[kk]);
 
     // O = scale (e^gamma Q S + M U), rows below n stored.
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      const char VFA_LDS* mr = smm + (32 * mt + l32) * S::TSTR + 8 * half;
+    for (int mt = 0; mt < 4; ++mt) {
+      const char VFA_LDS* mr = smm + (16 * mt + c16) * S::TSTR + 8 * g;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const bf16x8 mh = lds_perm(mr + 32 * kk), ml = lds_perm(mr + 2 * kC + 32 * kk);
-        qs[mt] = mfma(mh, uh[kk], qs[mt]);
-        qs[mt] = mfma(mh, ul[kk], qs[mt]);
-        qs[mt] = mfma(ml, uh[kk], qs[mt]);
+      for (int kk = 0; kk < 2; ++kk) {
+        const bf16x8 mh = lds_perm16(mr + 64 * kk), ml = lds_perm16(mr + 2 * kC + 64 * kk);
+        qs[mt] = mfma16(mh, uh[kk], qs[mt]);
+        qs[mt] = mfma16(mh, ul[kk], qs[mt]);
+        qs[mt] = mfma16(ml, uh[kk], qs[mt]);
       }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int ii = 32 * mt + 8 * (r >> 2) + 4 * half + (r & 3);
+      for (int r = 0; r < 4; ++r) {
+        const int ii = 16 * mt + 4 * g + r;
         if (ii < n) out[((size_t)(t0 + ii) * hv + h) * DV + col] = (bf16)(scale * qs[mt][r]);
       }
     }
@@ -457,13 +464,13 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_chunk_kernel(
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) st[dt][r] *= decay;
+      for (int r = 0; r < 4; ++r) st[dt][r] *= decay;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const char VFA_LDS* p = sk + (16 * kk + tr_key) * S::KSTR + tr_d * 2 + 64 * dt;
-        const bf16x8 a = lds_read_tr(p, p + 8 * S::KSTR);
-        st[dt] = mfma(a, wh[kk], st[dt]);
-        st[dt] = mfma(a, wl[kk], st[dt]);
+      for (int kk = 0; kk < 2; ++kk) {
+        const char VFA_LDS* p = sk + (32 * kk + tr_key) * S::KSTR + tr_d * 2 + 32 * dt;
+        const bf16x8 a = lds_read_tr(p, p + 16 * S::KSTR);
+        st[dt] = mfma16(a, wh[kk], st[dt]);
+        st[dt] = mfma16(a, wl[kk], st[dt]);
       }
     }
   }
@@ -472,8 +479,7 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_chunk_kernel(
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        s_final[sbase + (size_t)(32 * dt + 8 * (r >> 2) + 4 * half + (r & 3)) * DV] = st[dt][r];
+      for (int r = 0; r < 4; ++r) s_final[sbase + (size_t)(16 * dt + 4 * g + r) * DV] = st[dt][r];
   }
 }
 
@@ -506,8 +512,8 @@ int launch_gated_delta_chunked(const GatedDeltaArgs& a, int max_seqlen, void* wo
   bf16* wt = (bf16*)ws;
   bf16* wm = wt + rows;
   float* we = (float*)(wm + rows);
-  if (a.dk == 128) return a.dv == 128 ? launch_t<128, 4>(a, n_chunks, wt, wm, we) : launch_t<128, 2>(a, n_chunks, wt, wm, we);
-  return a.dv == 128 ? launch_t<64, 4>(a, n_chunks, wt, wm, we) : launch_t<64, 2>(a, n_chunks, wt, wm, we);
+  if (a.dk == 128) return a.dv == 128 ? launch_t<128, 8>(a, n_chunks, wt, wm, we) : launch_t<128, 4>(a, n_chunks, wt, wm, we);
+  return a.dv == 128 ? launch_t<64, 8>(a, n_chunks, wt, wm, we) : launch_t<64, 4>(a, n_chunks, wt, wm, we);
 }
 
 }  // namespace vfa
