@@ -17,8 +17,8 @@
 //                    T = (I + A)^-1 by forward substitution in fp32, then T and
 //                    M as bf16 hi / lo pairs and the two decay factors per token
 //                    into the workspace.
-//   gdn_chunk_kernel one workgroup per (sequence, value head), one wave per 16
-//                    state columns, chunks in order: y = K S and Q S, then
+//   gdn_chunk_kernel one workgroup per (sequence, value head, 64 state
+//                    columns), one wave per 16 columns, chunks in order: y = K S and Q S, then
 //                    U = T r with r = beta (V - e^gamma y), then M U for the
 //                    output and K^T U~ for the state.
 //
@@ -40,6 +40,8 @@ namespace vfa {
 namespace {
 
 constexpr int kC = 64;                  // tokens per chunk
+
+typedef __attribute__((__vector_size__(2 * sizeof(double)))) double f64x2;
 
 __device__ __forceinline__ bf16x8 join(bf16x4 a, bf16x4 b) {
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -65,12 +67,12 @@ __device__ __forceinline__ size_t ws_row(size_t t, int hv, int h) { return (t * 
 // ---------------------------------------------------------------------------
 // Phase 1: per (sequence, chunk, value head), independent of the state.
 template <int DK>
-__global__ __launch_bounds__(64) void gdn_prep_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void gdn_prep_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                       const float* __restrict__ g, const float* __restrict__ beta,
                                                       const int32_t* __restrict__ cu, int hqk, int hv, int n_chunks,
                                                       bf16* __restrict__ wt, bf16* __restrict__ wm,
                                                       float* __restrict__ we) {
-  __shared__ double sgam[kC];
+  __shared__ __attribute__((aligned(16))) double sgam[kC];
   __shared__ float sbeta[kC];
   __shared__ __attribute__((aligned(16))) float sat[kC][kC + 4];   // A transposed: sat[j][i] = A_ij
 
@@ -103,55 +105,89 @@ __global__ __launch_bounds__(64) void gdn_prep_kernel(const bf16* __restrict__ q
     we[2 * o + 1] = decay_factor(sgam[n - 1] - gl);   // e^(gamma_end - gamma_i)
   }
 
-  // K K^T and Q K^T (rows i, columns j; tile (1, 0) below the diagonal block).
-  f32x16 kk[3] = {}, qk[3] = {};                 // tiles (0,0), (1,0), (1,1)
-  const bf16* kr0 = k + ((size_t)(t0 + min(l32, n - 1)) * hqk + hk) * DK + 8 * half;
-  const bf16* kr1 = k + ((size_t)(t0 + min(32 + l32, n - 1)) * hqk + hk) * DK + 8 * half;
-  const bf16* qr0 = q + ((size_t)(t0 + min(l32, n - 1)) * hqk + hk) * DK + 8 * half;
-  const bf16* qr1 = q + ((size_t)(t0 + min(32 + l32, n - 1)) * hqk + hk) * DK + 8 * half;
+  // Products with rows m = key token j and columns n = token i, so that a
+  // lane (column i) holds four consecutive j of row i of A and M: K K^T (for
+  // A) and K Q^T (for M). Tiles (mt, nt) = (0,0), (0,1), (1,1); tile (1, 0)
+  // has j > i only, where both are zero. All operand loads are issued before
+  // the first product.
+  bf16x8 ka[2][DK / 16], qa[2][DK / 16];
 #pragma unroll
-  for (int ks = 0; ks < DK / 16; ++ks) {
-    const bf16x8 k0 = *(const bf16x8*)(kr0 + 16 * ks), k1 = *(const bf16x8*)(kr1 + 16 * ks);
-    const bf16x8 q0 = *(const bf16x8*)(qr0 + 16 * ks), q1 = *(const bf16x8*)(qr1 + 16 * ks);
-    kk[0] = mfma(k0, k0, kk[0]);
-    kk[1] = mfma(k1, k0, kk[1]);
-    kk[2] = mfma(k1, k1, kk[2]);
-    qk[0] = mfma(q0, k0, qk[0]);
-    qk[1] = mfma(q1, k0, qk[1]);
-    qk[2] = mfma(q1, k1, qk[2]);
+  for (int t = 0; t < 2; ++t) {
+    const size_t row = ((size_t)(t0 + min(32 * t + l32, n - 1)) * hqk + hk) * DK + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < DK / 16; ++ks) {
+      ka[t][ks] = *(const bf16x8*)(k + row + 16 * ks);
+      qa[t][ks] = *(const bf16x8*)(q + row + 16 * ks);
+    }
   }
+  // Every operand is consumed here, so all loads are in flight together and
+  // the products below wait on memory once (left alone, the compiler keeps
+  // only a few loads ahead of the products and pays several round trips).
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int ks = 0; ks < DK / 16; ++ks) __asm__ volatile("" ::"v"(ka[t][ks]), "v"(qa[t][ks]));
+  constexpr int kMt[3] = {0, 0, 1}, kNt[3] = {0, 1, 1};
+  f32x16 kk[3] = {}, kq[3] = {};
+#pragma unroll
+  for (int ks = 0; ks < DK / 16; ++ks)
+#pragma unroll
+    for (int tile = 0; tile < 3; ++tile) {
+      kk[tile] = mfma(ka[kMt[tile]][ks], ka[kNt[tile]][ks], kk[tile]);
+      kq[tile] = mfma(ka[kMt[tile]][ks], qa[kNt[tile]][ks], kq[tile]);
+    }
 
-  // A (into LDS) and M (hi / lo into the workspace), with the decay and masks.
-  constexpr int kMt[3] = {0, 1, 1}, kNt[3] = {0, 0, 1};
+  // A_ij = beta_i e^(gamma_i - gamma_j) k_i.k_j (j < i) into LDS as sat[j][i];
+  // M_ij = e^(gamma_i - gamma_j) q_i.k_j (j <= i), hi / lo, four consecutive
+  // columns per 8-byte store into the workspace.
 #pragma unroll
   for (int tile = 0; tile < 3; ++tile) {
-    const int j = 32 * kNt[tile] + l32;
-    const double gj = sgam[j];
+    const int i = 32 * kNt[tile] + l32;
+    const double gi = sgam[i];
+    const float bi = sbeta[i];
+    const bool live = i < n;
+    bf16* mrow = wm + ws_row(t0 + min(i, n - 1), hv, h);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int i = 32 * kMt[tile] + 8 * (r >> 2) + 4 * half + (r & 3);
-      const float d = (j <= i) ? decay_factor(sgam[i] - gj) : 0.f;
-      const bool live = i < n;
-      sat[j][i] = (live && j < i) ? sbeta[i] * d * kk[tile][r] : 0.f;
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int jb = 32 * kMt[tile] + 8 * g4 + 4 * half;
+      double gj[4];
+      *(f64x2*)&gj[0] = *(const f64x2*)&sgam[jb];
+      *(f64x2*)&gj[2] = *(const f64x2*)&sgam[jb + 2];
+      float mv[4];
+#pragma unroll
+      for (int z = 0; z < 4; ++z) {
+        const int r = 4 * g4 + z;
+        const int j = jb + z;
+        // Computed for every j and selected after (for j > i it may be inf,
+        // which the select drops): no branch around the fp64 difference.
+        const float e = decay_factor(gi - gj[z]);
+        const float d = (j <= i) ? e : 0.f;
+        sat[j][i] = (live && j < i) ? bi * d * kk[tile][r] : 0.f;
+        mv[z] = d * kq[tile][r];
+      }
+      const bf16x2 h01 = f32x2_to_bf16x2(mv[0], mv[1]), h23 = f32x2_to_bf16x2(mv[2], mv[3]);
+      const bf16x2 l01 = f32x2_to_bf16x2(mv[0] - (float)h01[0], mv[1] - (float)h01[1]);
+      const bf16x2 l23 = f32x2_to_bf16x2(mv[2] - (float)h23[0], mv[3] - (float)h23[1]);
       if (live) {
-        const float m = d * qk[tile][r];
-        const bf16 mh = (bf16)m;
-        bf16* row = wm + ws_row(t0 + i, hv, h);
-        row[j] = mh;
-        row[kC + j] = (bf16)(m - (float)mh);
+        const int j0 = 32 * kMt[tile] + 8 * g4 + 4 * half;
+        *(bf16x4*)(mrow + j0) = bf16x4{h01[0], h01[1], h23[0], h23[1]};
+        *(bf16x4*)(mrow + kC + j0) = bf16x4{l01[0], l01[1], l23[0], l23[1]};
       }
     }
   }
-  // Tile (0, 1) lies above the diagonal: A and M are zero there.
+  // Tile (1, 0): j >= 32 > i, zero in A and M.
+  {
+    const int i = l32;
+    bf16* mrow = wm + ws_row(t0 + min(i, n - 1), hv, h);
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int i = 8 * (r >> 2) + 4 * half + (r & 3);
-    const int j = 32 + l32;
-    sat[j][i] = 0.f;
-    if (i < n) {
-      bf16* row = wm + ws_row(t0 + i, hv, h);
-      row[j] = (bf16)0.f;
-      row[kC + j] = (bf16)0.f;
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int j0 = 32 + 8 * g4 + 4 * half;
+#pragma unroll
+      for (int z = 0; z < 4; ++z) sat[j0 + z][i] = 0.f;
+      if (i < n) {
+        *(bf16x4*)(mrow + j0) = bf16x4{};
+        *(bf16x4*)(mrow + kC + j0) = bf16x4{};
+      }
     }
   }
   __syncthreads();
@@ -193,8 +229,8 @@ __global__ __launch_bounds__(64) void gdn_prep_kernel(const bf16* __restrict__ q
 }
 
 // ---------------------------------------------------------------------------
-// Phase 2: per (sequence, value head), chunks in order; wave w owns state
-// columns 16 w .. 16 w + 15 (v_mfma_f32_16x16x32_bf16: lane (c16, g) holds
+// Phase 2: per (sequence, value head, 64-column group), chunks in order; the
+// four waves own 16 state columns each (v_mfma_f32_16x16x32_bf16: lane (c16, g) holds
 // k-slots 8 g + 0..7 of its row or column, and accumulator rows 4 g + 0..3).
 // Two 16-row accumulator tiles form one 32-deep B operand, k-slot 8 g + x
 // holding row {4 g + x, 16 + 4 g + x - 4}; memory-side A operands read their
@@ -202,11 +238,17 @@ __global__ __launch_bounds__(64) void gdn_prep_kernel(const bf16* __restrict__ q
 // LDS read pair 16 rows apart delivers it too. Each chunk's K, Q, T, M and V
 // rows (and the per-token beta and decay factors) are loaded into registers
 // one chunk ahead and stored to LDS after the barrier, so the chunk's chain of
-// products reads only LDS.
-template <int DK, int WAVES>
+// products reads only LDS. Splitting a head's Dv columns over workgroups
+// shortens the longest sequence's chain, which sets the kernel's duration:
+// each CU then carries half the per-chunk LDS reads and products, and two
+// such workgroups fit on a CU.
+constexpr int kChunkWaves = 4;
+constexpr int kGroupCols = kChunkWaves * 16;   // state columns per workgroup
+
+template <int DK>
 struct ChunkSmem {
-  static constexpr int THREADS = WAVES * 64;
-  static constexpr int DV = WAVES * 16;
+  static constexpr int THREADS = kChunkWaves * 64;
+  static constexpr int DV = kGroupCols;         // staged V columns
   // Row strides of 2 D + 16 bytes (D = 64 or 128): both the A-operand row
   // reads (lane (c16, g) at row c16, dword 2 g) and the transposed reads (rows
   // 4 g + 0..3, dwords 2 (i & 3)) then touch each of the 64 banks exactly
@@ -215,7 +257,7 @@ struct ChunkSmem {
   static constexpr int KSTR = DK * 2 + 16;     // K rows (row and transposed reads)
   static constexpr int QSTR = DK * 2 + 16;     // Q rows
   static constexpr int TSTR = 2 * kC * 2 + 16; // T and M rows (hi | lo)
-  static constexpr int VSTR = DV * 2 + 16;     // V rows (transposed reads)
+  static constexpr int VSTR = DV * 2 + 16;     // V rows of this group's columns (transposed reads)
   static constexpr int K_OFF = 0;
   static constexpr int Q_OFF = K_OFF + kC * KSTR;
   static constexpr int T_OFF = Q_OFF + kC * QSTR;
@@ -251,14 +293,14 @@ __device__ __forceinline__ void split_pair(const f32x4& t0, const f32x4& t1, bf1
   }
 }
 
-template <int DK, int WAVES>
-__global__ __launch_bounds__(WAVES * 64) void gdn_chunk_kernel(
+template <int DK, int DV>
+__global__ __launch_bounds__(kChunkWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void gdn_chunk_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ beta, const int32_t* __restrict__ cu, int hqk, int hv, float scale,
     const float* __restrict__ s_init, bf16* __restrict__ out, float* __restrict__ s_final,
     const bf16* __restrict__ wt, const bf16* __restrict__ wm, const float* __restrict__ we) {
-  using S = ChunkSmem<DK, WAVES>;
-  constexpr int DV = S::DV;
+  using S = ChunkSmem<DK>;
+  constexpr int NCG = DV / kGroupCols;  // column groups per head
   constexpr int NDT = DK / 16;          // 16-row tiles of the state
   __shared__ __attribute__((aligned(16))) char smem[S::BYTES];
   __shared__ __attribute__((aligned(16))) float se1[kC], se2[kC], sbt[kC];
@@ -269,15 +311,16 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_chunk_kernel(
   char VFA_LDS* smm = lds + S::M_OFF;
   char VFA_LDS* sv = lds + S::V_OFF;
 
-  const int h = blockIdx.x % hv;
-  const int b = blockIdx.x / hv;
+  const int cg = blockIdx.x % NCG;
+  const int h = (blockIdx.x / NCG) % hv;
+  const int b = blockIdx.x / (NCG * hv);
   const int hk = h / (hv / hqk);
   const int ts = cu[b];
   const int len = cu[b + 1] - ts;
   const int tid = threadIdx.x;
   const int lane = tid & 63, c16 = lane & 15, g = lane >> 4;
-  const int col0 = (tid >> 6) * 16;
-  const int col = col0 + c16;
+  const int lcol0 = (tid >> 6) * 16;    // first column of this wave within the group
+  const int col = cg * kGroupCols + lcol0 + c16;
 
   // Transposed reads: lane (c16, g) receives column c16 of a 16-wide block for
   // rows {4 g + 0..3} (first read) and {16 + 4 g + 0..3} (second, 16 rows on).
@@ -320,8 +363,8 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_chunk_kernel(
 #pragma unroll
     for (int i = 0; i < S::PV; ++i) {
       const int e = tid + i * S::THREADS;
-      const int r = min(e / (DV / 8), n - 1), c8 = e % (DV / 8);
-      pv[i] = *(const u32x4*)(v + ((size_t)(t0 + r) * hv + h) * DV + 8 * c8);
+      const int r = min(e / (S::DV / 8), n - 1), c8 = e % (S::DV / 8);
+      pv[i] = *(const u32x4*)(v + ((size_t)(t0 + r) * hv + h) * DV + cg * kGroupCols + 8 * c8);
     }
     if (tid < kC) {
       const bool ok = tid < n;
@@ -349,7 +392,7 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_chunk_kernel(
 #pragma unroll
     for (int i = 0; i < S::PV; ++i) {
       const int e = tid + i * S::THREADS;
-      const int r = e / (DV / 8), c8 = e % (DV / 8);
+      const int r = e / (S::DV / 8), c8 = e % (S::DV / 8);
       *(u32x4 VFA_LDS*)(sv + r * S::VSTR + 16 * c8) = pv[i];
     }
     if (tid < kC) {
@@ -394,7 +437,7 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_chunk_kernel(
     // comes through the transposed read, already in accumulator row order.
 #pragma unroll
     for (int s32 = 0; s32 < 2; ++s32) {
-      const char VFA_LDS* p = sv + (32 * s32 + tr_key) * S::VSTR + tr_d * 2 + 2 * col0;
+      const char VFA_LDS* p = sv + (32 * s32 + tr_key) * S::VSTR + tr_d * 2 + 2 * lcol0;
       const bf16x8 vv = lds_read_tr(p, p + 16 * S::VSTR);
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
@@ -483,16 +526,16 @@ __global__ __launch_bounds__(WAVES * 64) void gdn_chunk_kernel(
   }
 }
 
-template <int DK, int WAVES>
+template <int DK, int DV>
 int launch_t(const GatedDeltaArgs& a, int n_chunks, bf16* wt, bf16* wm, float* we) {
   const long long prep = (long long)a.batch * a.hv * n_chunks;
-  const long long main_blocks = (long long)a.batch * a.hv;
+  const long long main_blocks = (long long)a.batch * a.hv * (DV / kGroupCols);
   if (prep > 0x7fffffffLL || main_blocks > 0x7fffffffLL) return -1;
   hipStream_t s = (hipStream_t)a.stream;
   hipLaunchKernelGGL((gdn_prep_kernel<DK>), dim3((unsigned)prep), dim3(64), 0, s, (const bf16*)a.q,
                      (const bf16*)a.k, a.g, a.beta, a.cu, a.hqk, a.hv, n_chunks, wt, wm, we);
   if (hipGetLastError() != hipSuccess) return -1;
-  hipLaunchKernelGGL((gdn_chunk_kernel<DK, WAVES>), dim3((unsigned)main_blocks), dim3(WAVES * 64), 0, s,
+  hipLaunchKernelGGL((gdn_chunk_kernel<DK, DV>), dim3((unsigned)main_blocks), dim3(kChunkWaves * 64), 0, s,
                      (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.beta, a.cu, a.hqk, a.hv, a.scale,
                      a.s_init, (bf16*)a.out, a.s_final, (const bf16*)wt, (const bf16*)wm, (const float*)we);
   return hipGetLastError() == hipSuccess ? 0 : -1;
@@ -512,8 +555,8 @@ int launch_gated_delta_chunked(const GatedDeltaArgs& a, int max_seqlen, void* wo
   bf16* wt = (bf16*)ws;
   bf16* wm = wt + rows;
   float* we = (float*)(wm + rows);
-  if (a.dk == 128) return a.dv == 128 ? launch_t<128, 8>(a, n_chunks, wt, wm, we) : launch_t<128, 4>(a, n_chunks, wt, wm, we);
-  return a.dv == 128 ? launch_t<64, 8>(a, n_chunks, wt, wm, we) : launch_t<64, 4>(a, n_chunks, wt, wm, we);
+  if (a.dk == 128) return a.dv == 128 ? launch_t<128, 128>(a, n_chunks, wt, wm, we) : launch_t<128, 64>(a, n_chunks, wt, wm, we);
+  return a.dv == 128 ? launch_t<64, 128>(a, n_chunks, wt, wm, we) : launch_t<64, 64>(a, n_chunks, wt, wm, we);
 }
 
 }  // namespace vfa
