@@ -229,21 +229,25 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 }
 
 // ---------------------------------------------------------------------------
-// Phase 2: per (sequence, value head, 64-column group), chunks in order; the
-// four waves own 16 state columns each (v_mfma_f32_16x16x32_bf16: lane (c16, g) holds
-// k-slots 8 g + 0..7 of its row or column, and accumulator rows 4 g + 0..3).
-// Two 16-row accumulator tiles form one 32-deep B operand, k-slot 8 g + x
-// holding row {4 g + x, 16 + 4 g + x - 4}; memory-side A operands read their
-// k values in that order (two 8-byte runs 32 bytes apart), and the transposed
-// LDS read pair 16 rows apart delivers it too. Each chunk's K, Q, T, M and V
-// rows (and the per-token beta and decay factors) are loaded into registers
-// one chunk ahead and stored to LDS after the barrier, so the chunk's chain of
-// products reads only LDS. Splitting a head's Dv columns over workgroups
-// shortens the longest sequence's chain, which sets the kernel's duration:
-// each CU then carries half the per-chunk LDS reads and products, and two
-// such workgroups fit on a CU.
-constexpr int kChunkWaves = 4;
-constexpr int kGroupCols = kChunkWaves * 16;   // state columns per workgroup
+// Phase 2: per (sequence, value head, 64-column group), chunks in order. The
+// four "chain" waves own 16 state columns each and run the dependent chain
+// y = K S -> r -> U = T r -> S' = e^gamma_end S + K^T U~; four "output" waves,
+// one per chain wave, compute O = scale (e^gamma Q S + M U) for the same
+// columns from S and U that the chain waves leave in LDS already split into
+// bf16 hi / lo B operands. The output work then runs beside the chain instead
+// of lengthening it.
+//
+// Products use v_mfma_f32_16x16x32_bf16 (lane (c16, g) holds k-slots 8 g + 0..7
+// of its row or column, and accumulator rows 4 g + 0..3). Two 16-row
+// accumulator tiles form one 32-deep B operand, k-slot 8 g + x holding row
+// {4 g + x, 16 + 4 g + x - 4}; memory-side A operands read their k values in
+// that order (two 8-byte runs 32 bytes apart), and the transposed LDS read
+// pair 16 rows apart delivers it too. Each chunk's K, Q, T, M and V rows (and
+// the per-token beta and decay factors) are loaded into registers one chunk
+// ahead by all eight waves and stored to LDS after the barrier.
+constexpr int kChainWaves = 4;
+constexpr int kChunkWaves = 2 * kChainWaves;       // chain + output waves
+constexpr int kGroupCols = kChainWaves * 16;       // state columns per workgroup
 
 template <int DK>
 struct ChunkSmem {
@@ -263,7 +267,13 @@ struct ChunkSmem {
   static constexpr int T_OFF = Q_OFF + kC * QSTR;
   static constexpr int M_OFF = T_OFF + kC * TSTR;
   static constexpr int V_OFF = M_OFF + kC * TSTR;
-  static constexpr int BYTES = V_OFF + kC * VSTR;
+  // Hand-over buffers, one 16-byte B operand per lane: S (DK / 32 k steps, hi
+  // and lo) and U (2 k steps, hi and lo) per chain wave.
+  static constexpr int SB_OFF = V_OFF + kC * VSTR;
+  static constexpr int SB_WAVE = (DK / 32) * 2 * 64 * 16;
+  static constexpr int UB_OFF = SB_OFF + kChainWaves * SB_WAVE;
+  static constexpr int UB_WAVE = 2 * 2 * 64 * 16;
+  static constexpr int BYTES = UB_OFF + kChainWaves * UB_WAVE;
   // 16-byte pieces per thread for each staged tensor.
   static constexpr int PK = kC * DK / 8 / THREADS;
   static constexpr int PT = kC * (2 * kC) / 8 / THREADS;
@@ -302,6 +312,7 @@ __global__ __launch_bounds__(kChunkWaves * 64) __attribute__((amdgpu_waves_per_e
   using S = ChunkSmem<DK>;
   constexpr int NCG = DV / kGroupCols;  // column groups per head
   constexpr int NDT = DK / 16;          // 16-row tiles of the state
+  constexpr int NKS = DK / 32;          // 32-deep k steps over the state rows
   __shared__ __attribute__((aligned(16))) char smem[S::BYTES];
   __shared__ __attribute__((aligned(16))) float se1[kC], se2[kC], sbt[kC];
   char VFA_LDS* lds = (char VFA_LDS*)smem;
@@ -318,9 +329,17 @@ __global__ __launch_bounds__(kChunkWaves * 64) __attribute__((amdgpu_waves_per_e
   const int ts = cu[b];
   const int len = cu[b + 1] - ts;
   const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const bool chain = wave < kChainWaves;           // wave-uniform role
+  // Chain wave w and output wave w + 4 share a SIMD; the chain issues first.
+  if (chain) __builtin_amdgcn_s_setprio(1);
+  const int pw = wave % kChainWaves;               // column slot shared by a chain / output pair
   const int lane = tid & 63, c16 = lane & 15, g = lane >> 4;
-  const int lcol0 = (tid >> 6) * 16;    // first column of this wave within the group
+  const int lcol0 = pw * 16;                       // first column of the pair within the group
   const int col = cg * kGroupCols + lcol0 + c16;
+  // This pair's hand-over slots, indexed [k step][hi, lo][lane] of 16 bytes.
+  char VFA_LDS* sbuf = lds + S::SB_OFF + pw * S::SB_WAVE + lane * 16;
+  char VFA_LDS* ubuf = lds + S::UB_OFF + pw * S::UB_WAVE + lane * 16;
 
   // Transposed reads: lane (c16, g) receives column c16 of a 16-wide block for
   // rows {4 g + 0..3} (first read) and {16 + 4 g + 0..3} (second, 16 rows on).
@@ -328,14 +347,24 @@ __global__ __launch_bounds__(kChunkWaves * 64) __attribute__((amdgpu_waves_per_e
   const int tr_key = g * 4 + (tr_i >> 2);
   const int tr_d = 4 * (tr_i & 3);
 
-  // State rows d = 16 dt + 4 g + r, column col.
+  // Chain waves: state rows d = 16 dt + 4 g + r, column col; and its bf16
+  // hi / lo B operands, published to the output wave through sbuf.
   f32x4 st[NDT];
+  bf16x8 sh[NKS], sl[NKS];
   const size_t sbase = ((size_t)b * hv + h) * DK * DV + col;
+  if (chain) {
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt)
+    for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      st[dt][r] = s_init ? s_init[sbase + (size_t)(16 * dt + 4 * g + r) * DV] : 0.f;
+      for (int r = 0; r < 4; ++r)
+        st[dt][r] = s_init ? s_init[sbase + (size_t)(16 * dt + 4 * g + r) * DV] : 0.f;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      split_pair(st[2 * ks], st[2 * ks + 1], sh[ks], sl[ks]);
+      *(bf16x8 VFA_LDS*)(sbuf + (2 * ks) * 64 * 16) = sh[ks];
+      *(bf16x8 VFA_LDS*)(sbuf + (2 * ks + 1) * 64 * 16) = sl[ks];
+    }
+  }
 
   // Chunk loads into registers. Rows past the chunk's end repeat its last row
   // (finite values): their beta and decay factors are zero, so they add nothing.
@@ -408,117 +437,153 @@ __global__ __launch_bounds__(kChunkWaves * 64) __attribute__((amdgpu_waves_per_e
     const int t0 = ts + c0;
     __syncthreads();                    // the previous chunk's LDS reads are done
     store_chunk();
-    __syncthreads();
+    __syncthreads();                    // chunk staged; S of this chunk start in sbuf
     if (c0 + kC < len) load_chunk(c0 + kC);   // next chunk, in flight during this one
 
-    // S as B operands (32-deep k steps over the state rows), hi and lo.
-    bf16x8 sh[DK / 32], sl[DK / 32];
+    f32x4 qs[4];
+    if (chain) {
+      // y = K S (hi and lo); rows: chunk tokens 16 mt + 4 g + r.
+      f32x4 y[4] = {};
 #pragma unroll
-    for (int ks = 0; ks < DK / 32; ++ks) split_pair(st[2 * ks], st[2 * ks + 1], sh[ks], sl[ks]);
-
-    // y = K S and Q S (hi and lo); rows: chunk tokens 16 mt + 4 g + r.
-    f32x4 y[4] = {}, qs[4] = {};
+      for (int mt = 0; mt < 4; ++mt) {
+        const char VFA_LDS* kr = sk + (16 * mt + c16) * S::KSTR + 8 * g;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const char VFA_LDS* kr = sk + (16 * mt + c16) * S::KSTR + 8 * g;
-      const char VFA_LDS* qr = sq + (16 * mt + c16) * S::QSTR + 8 * g;
-#pragma unroll
-      for (int ks = 0; ks < DK / 32; ++ks) {
-        const bf16x8 ak = lds_perm16(kr + 64 * ks);
-        const bf16x8 aq = lds_perm16(qr + 64 * ks);
-        y[mt] = mfma16(ak, sh[ks], y[mt]);
-        y[mt] = mfma16(ak, sl[ks], y[mt]);
-        qs[mt] = mfma16(aq, sh[ks], qs[mt]);
-        qs[mt] = mfma16(aq, sl[ks], qs[mt]);
-      }
-    }
-
-    // r = beta (v - e^gamma y) in place, and the e^gamma scaling of Q S. V
-    // comes through the transposed read, already in accumulator row order.
-#pragma unroll
-    for (int s32 = 0; s32 < 2; ++s32) {
-      const char VFA_LDS* p = sv + (32 * s32 + tr_key) * S::VSTR + tr_d * 2 + 2 * lcol0;
-      const bf16x8 vv = lds_read_tr(p, p + 16 * S::VSTR);
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int mt = 2 * s32 + hh;
-        const int i0 = 16 * mt + 4 * g;
-        const f32x4 e1 = *(const f32x4*)&se1[i0];
-        const f32x4 bt = *(const f32x4*)&sbt[i0];
-#pragma unroll
-        for (int z = 0; z < 4; ++z) {
-          y[mt][z] = bt[z] * ((float)vv[4 * hh + z] - e1[z] * y[mt][z]);
-          qs[mt][z] *= e1[z];
+        for (int ks = 0; ks < NKS; ++ks) {
+          const bf16x8 ak = lds_perm16(kr + 64 * ks);
+          y[mt] = mfma16(ak, sh[ks], y[mt]);
+          y[mt] = mfma16(ak, sl[ks], y[mt]);
         }
       }
-    }
-    bf16x8 rh[2], rl[2];
+      // r = beta (v - e^gamma y) in place; V comes through the transposed read,
+      // already in accumulator row order.
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) split_pair(y[2 * kk], y[2 * kk + 1], rh[kk], rl[kk]);
-
-    // U = T r.
-    f32x4 u[4] = {};
+      for (int s32 = 0; s32 < 2; ++s32) {
+        const char VFA_LDS* p = sv + (32 * s32 + tr_key) * S::VSTR + tr_d * 2 + 2 * lcol0;
+        const bf16x8 vv = lds_read_tr(p, p + 16 * S::VSTR);
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const char VFA_LDS* tr = stt + (16 * mt + c16) * S::TSTR + 8 * g;
+        for (int hh = 0; hh < 2; ++hh) {
+          const int mt = 2 * s32 + hh;
+          const int i0 = 16 * mt + 4 * g;
+          const f32x4 e1 = *(const f32x4*)&se1[i0];
+          const f32x4 bt = *(const f32x4*)&sbt[i0];
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const bf16x8 th = lds_perm16(tr + 64 * kk), tl = lds_perm16(tr + 2 * kC + 64 * kk);
-        u[mt] = mfma16(th, rh[kk], u[mt]);
-        u[mt] = mfma16(th, rl[kk], u[mt]);
-        u[mt] = mfma16(tl, rh[kk], u[mt]);
+          for (int z = 0; z < 4; ++z) y[mt][z] = bt[z] * ((float)vv[4 * hh + z] - e1[z] * y[mt][z]);
+        }
       }
-    }
+      bf16x8 rh[2], rl[2];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) split_pair(y[2 * kk], y[2 * kk + 1], rh[kk], rl[kk]);
 
-    // U and U~ = e^(gamma_end - gamma) U as B operands.
-    bf16x8 uh[2], ul[2];
+      // U = T r, published (hi / lo) for the output wave's M U.
+      f32x4 u[4] = {};
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) split_pair(u[2 * kk], u[2 * kk + 1], uh[kk], ul[kk]);
+      for (int mt = 0; mt < 4; ++mt) {
+        const char VFA_LDS* tr = stt + (16 * mt + c16) * S::TSTR + 8 * g;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const f32x4 e2 = *(const f32x4*)&se2[16 * mt + 4 * g];
-#pragma unroll
-      for (int z = 0; z < 4; ++z) u[mt][z] *= e2[z];
-    }
-    bf16x8 wh[2], wl[2];
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) split_pair(u[2 * kk], u[2 * kk + 1], wh[kk], wl[kk]);
-
-    // O = scale (e^gamma Q S + M U), rows below n stored.
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const char VFA_LDS* mr = smm + (16 * mt + c16) * S::TSTR + 8 * g;
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const bf16x8 mh = lds_perm16(mr + 64 * kk), ml = lds_perm16(mr + 2 * kC + 64 * kk);
-        qs[mt] = mfma16(mh, uh[kk], qs[mt]);
-        qs[mt] = mfma16(mh, ul[kk], qs[mt]);
-        qs[mt] = mfma16(ml, uh[kk], qs[mt]);
+        for (int kk = 0; kk < 2; ++kk) {
+          const bf16x8 th = lds_perm16(tr + 64 * kk), tl = lds_perm16(tr + 2 * kC + 64 * kk);
+          u[mt] = mfma16(th, rh[kk], u[mt]);
+          u[mt] = mfma16(th, rl[kk], u[mt]);
+          u[mt] = mfma16(tl, rh[kk], u[mt]);
+        }
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int ii = 16 * mt + 4 * g + r;
-        if (ii < n) out[((size_t)(t0 + ii) * hv + h) * DV + col] = (bf16)(scale * qs[mt][r]);
+      for (int kk = 0; kk < 2; ++kk) {
+        bf16x8 uh, ul;
+        split_pair(u[2 * kk], u[2 * kk + 1], uh, ul);
+        *(bf16x8 VFA_LDS*)(ubuf + (2 * kk) * 64 * 16) = uh;
+        *(bf16x8 VFA_LDS*)(ubuf + (2 * kk + 1) * 64 * 16) = ul;
       }
-    }
+      // U~ = e^(gamma_end - gamma) U as B operands for the state update.
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const f32x4 e2 = *(const f32x4*)&se2[16 * mt + 4 * g];
+#pragma unroll
+        for (int z = 0; z < 4; ++z) u[mt][z] *= e2[z];
+      }
+      bf16x8 wh[2], wl[2];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) split_pair(u[2 * kk], u[2 * kk + 1], wh[kk], wl[kk]);
 
-    // S <- e^gamma_end S + K^T U~.
-    const float decay = se1[n - 1];
+      __syncthreads();                  // U published; the output waves are done with sbuf
+
+      // S <- e^gamma_end S + K^T U~, then its split for the next chunk (and
+      // for the output wave, which reads it after the next two barriers).
+      const float decay = se1[n - 1];
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
+      for (int dt = 0; dt < NDT; ++dt) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) st[dt][r] *= decay;
+        for (int r = 0; r < 4; ++r) st[dt][r] *= decay;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const char VFA_LDS* p = sk + (32 * kk + tr_key) * S::KSTR + tr_d * 2 + 32 * dt;
+          const bf16x8 a = lds_read_tr(p, p + 16 * S::KSTR);
+          st[dt] = mfma16(a, wh[kk], st[dt]);
+          st[dt] = mfma16(a, wl[kk], st[dt]);
+        }
+      }
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        split_pair(st[2 * ks], st[2 * ks + 1], sh[ks], sl[ks]);
+        *(bf16x8 VFA_LDS*)(sbuf + (2 * ks) * 64 * 16) = sh[ks];
+        *(bf16x8 VFA_LDS*)(sbuf + (2 * ks + 1) * 64 * 16) = sl[ks];
+      }
+    } else {
+      // Q S from the chain wave's published S (hi and lo), scaled by e^gamma.
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        qs[mt] = f32x4{};
+        const char VFA_LDS* qr = sq + (16 * mt + c16) * S::QSTR + 8 * g;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          const bf16x8 aq = lds_perm16(qr + 64 * ks);
+          qs[mt] = mfma16(aq, *(const bf16x8 VFA_LDS*)(sbuf + (2 * ks) * 64 * 16), qs[mt]);
+          qs[mt] = mfma16(aq, *(const bf16x8 VFA_LDS*)(sbuf + (2 * ks + 1) * 64 * 16), qs[mt]);
+        }
+        const f32x4 e1 = *(const f32x4*)&se1[16 * mt + 4 * g];
+#pragma unroll
+        for (int z = 0; z < 4; ++z) qs[mt][z] *= e1[z];
+      }
+
+      __syncthreads();                  // U published by the chain wave
+
+      // O = scale (e^gamma Q S + M U), rows below n stored (without a per-row
+      // test on full chunks, so the stores do not split the code into blocks).
+      bf16x8 uh[2], ul[2];
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const char VFA_LDS* p = sk + (32 * kk + tr_key) * S::KSTR + tr_d * 2 + 32 * dt;
-        const bf16x8 a = lds_read_tr(p, p + 16 * S::KSTR);
-        st[dt] = mfma16(a, wh[kk], st[dt]);
-        st[dt] = mfma16(a, wl[kk], st[dt]);
+        uh[kk] = *(const bf16x8 VFA_LDS*)(ubuf + (2 * kk) * 64 * 16);
+        ul[kk] = *(const bf16x8 VFA_LDS*)(ubuf + (2 * kk + 1) * 64 * 16);
+      }
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const char VFA_LDS* mr = smm + (16 * mt + c16) * S::TSTR + 8 * g;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const bf16x8 mh = lds_perm16(mr + 64 * kk), ml = lds_perm16(mr + 2 * kC + 64 * kk);
+          qs[mt] = mfma16(mh, uh[kk], qs[mt]);
+          qs[mt] = mfma16(mh, ul[kk], qs[mt]);
+          qs[mt] = mfma16(ml, uh[kk], qs[mt]);
+        }
+      }
+      bf16* orow = out + ((size_t)(t0 + 4 * g) * hv + h) * DV + col;   // row 4 g of the chunk
+      const size_t ostride = (size_t)hv * DV;                           // elements per token
+      if (n == kC) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) orow[(16 * mt + r) * ostride] = (bf16)(scale * qs[mt][r]);
+      } else {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (16 * mt + 4 * g + r < n) orow[(16 * mt + r) * ostride] = (bf16)(scale * qs[mt][r]);
       }
     }
   }
 
-  if (s_final) {
+  if (chain && s_final) {
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
