@@ -57,6 +57,24 @@ __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// Workgroup id -> (item, inner) with the `inner` workgroups of one item on one
+// XCD (workgroups are dispatched round-robin over the 8 XCDs), 8 ids apart, so
+// they share that XCD's L2: the value heads of one query / key head read the
+// same K and Q rows, the column groups of one head the same staged chunks.
+// Bijective on [0, items * inner); the last items % 8 items keep plain order.
+__device__ __forceinline__ void xcd_decode(int idx, int items, int inner, int& item, int& in) {
+  const int full = (items / 8) * 8 * inner;
+  if (idx < full) {
+    const int slot = idx / 8;
+    item = (slot / inner) * 8 + idx % 8;
+    in = slot % inner;
+  } else {
+    const int r = idx - full;
+    item = (items / 8) * 8 + r / inner;
+    in = r % inner;
+  }
+}
+
 // e^x for a log decay held in fp64: x rounded to fp32, then the hardware exp2.
 __device__ __forceinline__ float decay_factor(double x) { return fast_exp2((float)x * kLog2e); }
 
@@ -76,14 +94,18 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   __shared__ float sbeta[kC];
   __shared__ __attribute__((aligned(16))) float sat[kC][kC + 4];   // A transposed: sat[j][i] = A_ij
 
-  const int c = blockIdx.x % n_chunks;
-  const int h = (blockIdx.x / n_chunks) % hv;
-  const int b = blockIdx.x / (n_chunks * hv);
+  const int rep_v = hv / hqk;           // value heads per query / key head
+  int item, vi;
+  xcd_decode(blockIdx.x, gridDim.x / rep_v, rep_v, item, vi);
+  const int hk0 = item % hqk;
+  const int c = (item / hqk) % n_chunks;
+  const int b = item / (hqk * n_chunks);
+  const int h = hk0 * rep_v + vi;
   const int len = cu[b + 1] - cu[b];
   if (c * kC >= len) return;
   const int t0 = cu[b] + c * kC;
   const int n = min(kC, len - c * kC);
-  const int hk = h / (hv / hqk);
+  const int hk = hk0;
   const int lane = threadIdx.x;
   const int l32 = lane & 31, half = lane >> 5;
 
@@ -322,9 +344,10 @@ __global__ __launch_bounds__(kChunkWaves * 64) __attribute__((amdgpu_waves_per_e
   char VFA_LDS* smm = lds + S::M_OFF;
   char VFA_LDS* sv = lds + S::V_OFF;
 
-  const int cg = blockIdx.x % NCG;
-  const int h = (blockIdx.x / NCG) % hv;
-  const int b = blockIdx.x / (NCG * hv);
+  int item, cg;
+  xcd_decode(blockIdx.x, gridDim.x / NCG, NCG, item, cg);
+  const int h = item % hv;
+  const int b = item / hv;
   const int hk = h / (hv / hqk);
   const int ts = cu[b];
   const int len = cu[b + 1] - ts;
