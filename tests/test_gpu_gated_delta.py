@@ -71,6 +71,53 @@ def test_gated_delta_parity(name):
     check_close(f"{name}_state", host64(fin), f_ref, 1e-4, 1e-4)
 
 
+GATE_CASES = {
+    # name: how g and beta are replaced (the rest as make_gated_delta draws it)
+    "strong_decay": "g uniform in [-8, 0): e^gamma underflows to 0 inside a 64-token chunk",
+    "no_decay": "g = 0: the plain delta rule",
+    "beta_extremes": "beta exactly 0 or 1, alternating per token",
+}
+
+
+@pytest.mark.parametrize("name", sorted(GATE_CASES))
+def test_gated_delta_gate_extremes(name):
+    """Both paths against the oracle with gates the default draw never makes. The chunked path takes
+    decay factors from fp64 differences of the cumulative log decay, so factors that underflow in fp32
+    stay exact zeros rather than 0/0."""
+    torch = need_gpu()
+    lens = [200, 13, 64, 1]
+    p = make_gated_delta(lens, 2, 4, 128, 128, seed=95)
+    rng = np.random.default_rng(96)
+    if name == "strong_decay":
+        p.g[:] = (-8.0 * rng.random(p.g.shape)).astype(np.float32)
+    elif name == "no_decay":
+        p.g[:] = 0.0
+    else:
+        p.beta[:] = (np.arange(p.beta.shape[0])[:, None] % 2).astype(np.float32)
+    s0 = rng.standard_normal((len(lens), 4, 128, 128)).astype(np.float32) * 0.5
+    print(f"[case] gated_delta gates {name}: {GATE_CASES[name]}", flush=True)
+    x = dev_inputs(p)
+    o_ref, f_ref = oracle.gated_delta_rule(p.q, p.k, p.v, p.g, p.beta, p.cu_seqlens, p.scale, initial_state=s0)
+    for ms in (max(lens), 16):                       # chunked path, then token by token on the short ones
+        if ms == 16:
+            keep = [b for b, n in enumerate(lens) if n <= 16]
+            idx = np.concatenate([np.arange(p.cu_seqlens[b], p.cu_seqlens[b + 1]) for b in keep])
+            ii = torch.from_numpy(idx).cuda()
+            cu = torch.from_numpy(np.r_[0, np.cumsum([lens[b] for b in keep])].astype(np.int32)).cuda()
+            out, fin = vfa.gated_delta_rule_fwd(x["q"][ii].contiguous(), x["k"][ii].contiguous(), x["v"][ii].contiguous(),
+                                                x["g"][ii].contiguous(), x["beta"][ii].contiguous(), cu, 16,
+                                                scale=p.scale, initial_state=torch.from_numpy(s0[keep]).cuda(),
+                                                output_final_state=True)
+            want_o, want_f = o_ref[idx], f_ref[keep]
+        else:
+            out, fin = vfa.gated_delta_rule_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["cu"], ms, scale=p.scale,
+                                                initial_state=torch.from_numpy(s0).cuda(), output_final_state=True)
+            want_o, want_f = o_ref, f_ref
+        torch.cuda.synchronize()
+        check_close(f"{name}_ms{ms}_out", host64(out), want_o, 2.0 ** -7, 1e-4)
+        check_close(f"{name}_ms{ms}_state", host64(fin), want_f, 1e-4, 1e-4)
+
+
 def _continuation(lengths, split, seed):
     """Runs the packed sequences whole, then as two calls (the first `split[b]` tokens of each sequence,
     then the rest from the first call's final state); returns both outputs and final states."""
