@@ -56,6 +56,8 @@ def main(src, dst):
               "32 query columns, D=128, causal.",
               "  attn_decode_split_kernel<D, CAUSAL, PAGED, OutT>: ILi128ELb1ELb0 = contiguous decode (bench extra "
               "'decode'), ILi128ELb1ELb1 = paged decode (extras 'paged_decode_p16' and '_p128', one row for both).",
+              "  gdn_prep_kernel<DK> then gdn_chunk_kernel<DK, DV>: one gated delta rule call (extra "
+              "'gated_delta_rule', chunked form, Dk = Dv = 128).",
               f"headline kernel: {len(head_us)} launches = {warmup} warm-up + {steps} timed + the later extras' "
               "launches of the same kernel (none).",
               f"agreement: the {steps} timed launches average {trace_avg:.1f} us in this trace; bench.py's HIP events "
@@ -114,7 +116,9 @@ def main(src, dst):
         if HEAD in name:
             rec = (sum(fetch[name]) / len(fetch[name]), sum(write[name]) / len(write[name]), f_b, w_b)
     tl += ["", "attn_update_kernel<float, 128, 8, 1> runs the 2048-row merge shape (cold and warm calls "
-           "averaged, plus the 4x sweep point); <..., 2> the 16x and 64x sweep points (two rows per thread)."]
+           "averaged, plus the 4x sweep point); <..., 2> the 16x and 64x sweep points (two rows per thread).",
+           "gdn_prep_kernel writes the per-chunk T and M rows and decay factors (520 B per token and value head); "
+           "gdn_chunk_kernel reads them back with the chunk's K, Q and V and writes the output."]
     open(os.path.join(dst, "bench_kernels.hbm_traffic.txt"), "w").write("\n".join(tl) + "\n")
 
     sha = hashlib.sha256(open(os.path.join(repo, "varlen_flash_attention_amd", "csrc", "attn_fwd_bf16.hip"),
