@@ -256,24 +256,29 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 // y = K S -> r -> U = T r -> S' = e^gamma_end S + K^T U~; four "output" waves,
 // one per chain wave, compute O = scale (e^gamma Q S + M U) for the same
 // columns from S and U that the chain waves leave in LDS already split into
-// bf16 hi / lo B operands. The output work then runs beside the chain instead
-// of lengthening it.
+// bf16 hi / lo B operands. Each role stages what it reads: during chunk c the
+// chain waves load chunk c+1's K, T and V rows into registers and store them
+// after their state update (K into the second of two buffers, since the
+// update still reads this chunk's K); the output waves do the same for Q, M
+// and the per-token beta and decay factors after their stores, having taken
+// their M operands into registers before the mid-chunk barrier. Per chunk:
+// barrier A (chunk staged, S published), chain y, r, U / output Q S, barrier
+// B (U published), chain state update and staging / output M U, stores and
+// staging.
 //
 // Products use v_mfma_f32_16x16x32_bf16 (lane (c16, g) holds k-slots 8 g + 0..7
 // of its row or column, and accumulator rows 4 g + 0..3). Two 16-row
 // accumulator tiles form one 32-deep B operand, k-slot 8 g + x holding row
 // {4 g + x, 16 + 4 g + x - 4}; memory-side A operands read their k values in
 // that order (two 8-byte runs 32 bytes apart), and the transposed LDS read
-// pair 16 rows apart delivers it too. Each chunk's K, Q, T, M and V rows (and
-// the per-token beta and decay factors) are loaded into registers one chunk
-// ahead by all eight waves and stored to LDS after the barrier.
+// pair 16 rows apart delivers it too.
 constexpr int kChainWaves = 4;
 constexpr int kChunkWaves = 2 * kChainWaves;       // chain + output waves
 constexpr int kGroupCols = kChainWaves * 16;       // state columns per workgroup
 
 template <int DK>
 struct ChunkSmem {
-  static constexpr int THREADS = kChunkWaves * 64;
+  static constexpr int STAGERS = kChainWaves * 64;  // threads of one role (each role stages its tensors)
   static constexpr int DV = kGroupCols;         // staged V columns
   // Row strides of 2 D + 16 bytes (D = 64 or 128): both the A-operand row
   // reads (lane (c16, g) at row c16, dword 2 g) and the transposed reads (rows
@@ -284,8 +289,9 @@ struct ChunkSmem {
   static constexpr int QSTR = DK * 2 + 16;     // Q rows
   static constexpr int TSTR = 2 * kC * 2 + 16; // T and M rows (hi | lo)
   static constexpr int VSTR = DV * 2 + 16;     // V rows of this group's columns (transposed reads)
-  static constexpr int K_OFF = 0;
-  static constexpr int Q_OFF = K_OFF + kC * KSTR;
+  static constexpr int K_OFF = 0;              // two K buffers (chunk parity)
+  static constexpr int KBUF = kC * KSTR;
+  static constexpr int Q_OFF = K_OFF + 2 * KBUF;
   static constexpr int T_OFF = Q_OFF + kC * QSTR;
   static constexpr int M_OFF = T_OFF + kC * TSTR;
   static constexpr int V_OFF = M_OFF + kC * TSTR;
@@ -296,12 +302,12 @@ struct ChunkSmem {
   static constexpr int UB_OFF = SB_OFF + kChainWaves * SB_WAVE;
   static constexpr int UB_WAVE = 2 * 2 * 64 * 16;
   static constexpr int BYTES = UB_OFF + kChainWaves * UB_WAVE;
-  // 16-byte pieces per thread for each staged tensor.
-  static constexpr int PK = kC * DK / 8 / THREADS;
-  static constexpr int PT = kC * (2 * kC) / 8 / THREADS;
-  static constexpr int PV = kC * DV / 8 / THREADS;
-  static_assert(PK * THREADS * 8 == kC * DK && PT * THREADS * 8 == kC * 2 * kC && PV * THREADS * 8 == kC * DV,
-                "pieces must split evenly over the workgroup");
+  // 16-byte pieces per staging thread for each staged tensor.
+  static constexpr int PK = kC * DK / 8 / STAGERS;
+  static constexpr int PT = kC * (2 * kC) / 8 / STAGERS;
+  static constexpr int PV = kC * DV / 8 / STAGERS;
+  static_assert(PK * STAGERS * 8 == kC * DK && PT * STAGERS * 8 == kC * 2 * kC && PV * STAGERS * 8 == kC * DV,
+                "pieces must split evenly over the staging threads");
 };
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -338,7 +344,6 @@ __global__ __launch_bounds__(kChunkWaves * 64) __attribute__((amdgpu_waves_per_e
   __shared__ __attribute__((aligned(16))) char smem[S::BYTES];
   __shared__ __attribute__((aligned(16))) float se1[kC], se2[kC], sbt[kC];
   char VFA_LDS* lds = (char VFA_LDS*)smem;
-  char VFA_LDS* sk = lds + S::K_OFF;
   char VFA_LDS* sq = lds + S::Q_OFF;
   char VFA_LDS* stt = lds + S::T_OFF;
   char VFA_LDS* smm = lds + S::M_OFF;
@@ -357,6 +362,7 @@ __global__ __launch_bounds__(kChunkWaves * 64) __attribute__((amdgpu_waves_per_e
   // Chain wave w and output wave w + 4 share a SIMD; the chain issues first.
   if (chain) __builtin_amdgcn_s_setprio(1);
   const int pw = wave % kChainWaves;               // column slot shared by a chain / output pair
+  const int stid = tid % (kChainWaves * 64);       // staging thread index within the role
   const int lane = tid & 63, c16 = lane & 15, g = lane >> 4;
   const int lcol0 = pw * 16;                       // first column of the pair within the group
   const int col = cg * kGroupCols + lcol0 + c16;
@@ -389,82 +395,106 @@ __global__ __launch_bounds__(kChunkWaves * 64) __attribute__((amdgpu_waves_per_e
     }
   }
 
-  // Chunk loads into registers. Rows past the chunk's end repeat its last row
-  // (finite values): their beta and decay factors are zero, so they add nothing.
-  u32x4 pk[S::PK], pq[S::PK], pt[S::PT], pm[S::PT], pv[S::PV];
-  float pe1 = 0.f, pe2 = 0.f, pbt = 0.f;
-  auto load_chunk = [&](int c0) __attribute__((always_inline)) {
+  // Staging. Rows past a chunk's end repeat its last row (finite values):
+  // their beta and decay factors are zero, so they add nothing. Chain waves:
+  // K, T, V; output waves: Q, M and the factors.
+  u32x4 pk[S::PK], pt[S::PT], pv[S::PV];      // chain
+  u32x4 pq[S::PK], pm[S::PT];                  // output
+  float pe1 = 0.f, pe2 = 0.f, pbt = 0.f;      // output
+  auto load_chain = [&](int c0) __attribute__((always_inline)) {
     const int n = min(kC, len - c0);
     const int t0 = ts + c0;
 #pragma unroll
     for (int i = 0; i < S::PK; ++i) {
-      const int e = tid + i * S::THREADS;
+      const int e = stid + i * S::STAGERS;
       const int r = min(e / (DK / 8), n - 1), c8 = e % (DK / 8);
-      const size_t o = ((size_t)(t0 + r) * hqk + hk) * DK + 8 * c8;
-      pk[i] = *(const u32x4*)(k + o);
-      pq[i] = *(const u32x4*)(q + o);
+      pk[i] = *(const u32x4*)(k + ((size_t)(t0 + r) * hqk + hk) * DK + 8 * c8);
     }
 #pragma unroll
     for (int i = 0; i < S::PT; ++i) {
-      const int e = tid + i * S::THREADS;
+      const int e = stid + i * S::STAGERS;
       const int r = min(e / (2 * kC / 8), n - 1), c8 = e % (2 * kC / 8);
-      const size_t o = ws_row(t0 + r, hv, h) + 8 * c8;
-      pt[i] = *(const u32x4*)(wt + o);
-      pm[i] = *(const u32x4*)(wm + o);
+      pt[i] = *(const u32x4*)(wt + ws_row(t0 + r, hv, h) + 8 * c8);
     }
 #pragma unroll
     for (int i = 0; i < S::PV; ++i) {
-      const int e = tid + i * S::THREADS;
+      const int e = stid + i * S::STAGERS;
       const int r = min(e / (S::DV / 8), n - 1), c8 = e % (S::DV / 8);
       pv[i] = *(const u32x4*)(v + ((size_t)(t0 + r) * hv + h) * DV + cg * kGroupCols + 8 * c8);
     }
-    if (tid < kC) {
-      const bool ok = tid < n;
-      const size_t o = (size_t)(t0 + (ok ? tid : 0)) * hv + h;
+  };
+  auto store_chain = [&](int parity) __attribute__((always_inline)) {
+    char VFA_LDS* skw = lds + S::K_OFF + parity * S::KBUF;
+#pragma unroll
+    for (int i = 0; i < S::PK; ++i) {
+      const int e = stid + i * S::STAGERS;
+      *(u32x4 VFA_LDS*)(skw + (e / (DK / 8)) * S::KSTR + 16 * (e % (DK / 8))) = pk[i];
+    }
+#pragma unroll
+    for (int i = 0; i < S::PT; ++i) {
+      const int e = stid + i * S::STAGERS;
+      *(u32x4 VFA_LDS*)(stt + (e / (2 * kC / 8)) * S::TSTR + 16 * (e % (2 * kC / 8))) = pt[i];
+    }
+#pragma unroll
+    for (int i = 0; i < S::PV; ++i) {
+      const int e = stid + i * S::STAGERS;
+      *(u32x4 VFA_LDS*)(sv + (e / (S::DV / 8)) * S::VSTR + 16 * (e % (S::DV / 8))) = pv[i];
+    }
+  };
+  auto load_out = [&](int c0) __attribute__((always_inline)) {
+    const int n = min(kC, len - c0);
+    const int t0 = ts + c0;
+#pragma unroll
+    for (int i = 0; i < S::PK; ++i) {
+      const int e = stid + i * S::STAGERS;
+      const int r = min(e / (DK / 8), n - 1), c8 = e % (DK / 8);
+      pq[i] = *(const u32x4*)(q + ((size_t)(t0 + r) * hqk + hk) * DK + 8 * c8);
+    }
+#pragma unroll
+    for (int i = 0; i < S::PT; ++i) {
+      const int e = stid + i * S::STAGERS;
+      const int r = min(e / (2 * kC / 8), n - 1), c8 = e % (2 * kC / 8);
+      pm[i] = *(const u32x4*)(wm + ws_row(t0 + r, hv, h) + 8 * c8);
+    }
+    if (stid < kC) {
+      const bool ok = stid < n;
+      const size_t o = (size_t)(t0 + (ok ? stid : 0)) * hv + h;
       pe1 = ok ? we[2 * o] : 0.f;
       pe2 = ok ? we[2 * o + 1] : 0.f;
       pbt = ok ? beta[o] : 0.f;
     }
   };
-  auto store_chunk = [&]() __attribute__((always_inline)) {
+  auto store_out = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < S::PK; ++i) {
-      const int e = tid + i * S::THREADS;
-      const int r = e / (DK / 8), c8 = e % (DK / 8);
-      *(u32x4 VFA_LDS*)(sk + r * S::KSTR + 16 * c8) = pk[i];
-      *(u32x4 VFA_LDS*)(sq + r * S::QSTR + 16 * c8) = pq[i];
+      const int e = stid + i * S::STAGERS;
+      *(u32x4 VFA_LDS*)(sq + (e / (DK / 8)) * S::QSTR + 16 * (e % (DK / 8))) = pq[i];
     }
 #pragma unroll
     for (int i = 0; i < S::PT; ++i) {
-      const int e = tid + i * S::THREADS;
-      const int r = e / (2 * kC / 8), c8 = e % (2 * kC / 8);
-      *(u32x4 VFA_LDS*)(stt + r * S::TSTR + 16 * c8) = pt[i];
-      *(u32x4 VFA_LDS*)(smm + r * S::TSTR + 16 * c8) = pm[i];
+      const int e = stid + i * S::STAGERS;
+      *(u32x4 VFA_LDS*)(smm + (e / (2 * kC / 8)) * S::TSTR + 16 * (e % (2 * kC / 8))) = pm[i];
     }
-#pragma unroll
-    for (int i = 0; i < S::PV; ++i) {
-      const int e = tid + i * S::THREADS;
-      const int r = e / (S::DV / 8), c8 = e % (S::DV / 8);
-      *(u32x4 VFA_LDS*)(sv + r * S::VSTR + 16 * c8) = pv[i];
-    }
-    if (tid < kC) {
-      se1[tid] = pe1;
-      se2[tid] = pe2;
-      sbt[tid] = pbt;
+    if (stid < kC) {
+      se1[stid] = pe1;
+      se2[stid] = pe2;
+      sbt[stid] = pbt;
     }
   };
 
-  if (len > 0) load_chunk(0);
-  for (int c0 = 0; c0 < len; c0 += kC) {
-    const int n = min(kC, len - c0);
-    const int t0 = ts + c0;
-    __syncthreads();                    // the previous chunk's LDS reads are done
-    store_chunk();
-    __syncthreads();                    // chunk staged; S of this chunk start in sbuf
-    if (c0 + kC < len) load_chunk(c0 + kC);   // next chunk, in flight during this one
+  // The two roles run separate loops (so that neither holds the other's
+  // registers), each with the same two barriers per chunk.
+  if (chain) {
+    if (len > 0) {
+      load_chain(0);
+      store_chain(0);
+    }
+    for (int c0 = 0; c0 < len; c0 += kC) {
+      const int n = min(kC, len - c0);
+      const char VFA_LDS* sk = lds + S::K_OFF + ((c0 / kC) & 1) * S::KBUF;   // this chunk's K
+      __syncthreads();                  // A: chunk staged, S of this chunk start in sbuf
+      if (c0 + kC < len) load_chain(c0 + kC);   // next chunk, in flight during this one
 
-    f32x4 qs[4];
-    if (chain) {
       // y = K S (hi and lo); rows: chunk tokens 16 mt + 4 g + r.
       f32x4 y[4] = {};
 #pragma unroll
@@ -517,7 +547,8 @@ __global__ __launch_bounds__(kChunkWaves * 64) __attribute__((amdgpu_waves_per_e
         *(bf16x8 VFA_LDS*)(ubuf + (2 * kk) * 64 * 16) = uh;
         *(bf16x8 VFA_LDS*)(ubuf + (2 * kk + 1) * 64 * 16) = ul;
       }
-      // U~ = e^(gamma_end - gamma) U as B operands for the state update.
+      // U~ = e^(gamma_end - gamma) U as B operands for the state update; the
+      // decay is read now, before the staging after barrier B overwrites it.
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         const f32x4 e2 = *(const f32x4*)&se2[16 * mt + 4 * g];
@@ -527,12 +558,12 @@ __global__ __launch_bounds__(kChunkWaves * 64) __attribute__((amdgpu_waves_per_e
       bf16x8 wh[2], wl[2];
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) split_pair(u[2 * kk], u[2 * kk + 1], wh[kk], wl[kk]);
-
-      __syncthreads();                  // U published; the output waves are done with sbuf
-
-      // S <- e^gamma_end S + K^T U~, then its split for the next chunk (and
-      // for the output wave, which reads it after the next two barriers).
       const float decay = se1[n - 1];
+
+      __syncthreads();                  // B: U published; the output waves are done with sbuf
+
+      // S <- e^gamma_end S + K^T U~ (this chunk's K buffer, which the staging
+      // of the next chunk does not touch), then its split for the next chunk.
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
 #pragma unroll
@@ -551,8 +582,23 @@ __global__ __launch_bounds__(kChunkWaves * 64) __attribute__((amdgpu_waves_per_e
         *(bf16x8 VFA_LDS*)(sbuf + (2 * ks) * 64 * 16) = sh[ks];
         *(bf16x8 VFA_LDS*)(sbuf + (2 * ks + 1) * 64 * 16) = sl[ks];
       }
-    } else {
+      // Stage the next chunk's K (other buffer), T and V: this wave's reads of
+      // this chunk's T and V ended before barrier B.
+      if (c0 + kC < len) store_chain(((c0 / kC) + 1) & 1);
+    }
+  } else {
+    if (len > 0) {
+      load_out(0);
+      store_out();
+    }
+    for (int c0 = 0; c0 < len; c0 += kC) {
+      const int n = min(kC, len - c0);
+      const int t0 = ts + c0;
+      __syncthreads();                  // A: chunk staged, S of this chunk start in sbuf
+      if (c0 + kC < len) load_out(c0 + kC);     // next chunk, in flight during this one
+
       // Q S from the chain wave's published S (hi and lo), scaled by e^gamma.
+      f32x4 qs[4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         qs[mt] = f32x4{};
@@ -567,8 +613,19 @@ __global__ __launch_bounds__(kChunkWaves * 64) __attribute__((amdgpu_waves_per_e
 #pragma unroll
         for (int z = 0; z < 4; ++z) qs[mt][z] *= e1[z];
       }
+      // M operands into registers now: the staging after barrier B overwrites M.
+      bf16x8 mh[4][2], ml[4][2];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const char VFA_LDS* mr = smm + (16 * mt + c16) * S::TSTR + 8 * g;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          mh[mt][kk] = lds_perm16(mr + 64 * kk);
+          ml[mt][kk] = lds_perm16(mr + 2 * kC + 64 * kk);
+        }
+      }
 
-      __syncthreads();                  // U published by the chain wave
+      __syncthreads();                  // B: U published by the chain wave
 
       // O = scale (e^gamma Q S + M U), rows below n stored (without a per-row
       // test on full chunks, so the stores do not split the code into blocks).
@@ -579,16 +636,13 @@ __global__ __launch_bounds__(kChunkWaves * 64) __attribute__((amdgpu_waves_per_e
         ul[kk] = *(const bf16x8 VFA_LDS*)(ubuf + (2 * kk + 1) * 64 * 16);
       }
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const char VFA_LDS* mr = smm + (16 * mt + c16) * S::TSTR + 8 * g;
+      for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-          const bf16x8 mh = lds_perm16(mr + 64 * kk), ml = lds_perm16(mr + 2 * kC + 64 * kk);
-          qs[mt] = mfma16(mh, uh[kk], qs[mt]);
-          qs[mt] = mfma16(mh, ul[kk], qs[mt]);
-          qs[mt] = mfma16(ml, uh[kk], qs[mt]);
+          qs[mt] = mfma16(mh[mt][kk], uh[kk], qs[mt]);
+          qs[mt] = mfma16(mh[mt][kk], ul[kk], qs[mt]);
+          qs[mt] = mfma16(ml[mt][kk], uh[kk], qs[mt]);
         }
-      }
       bf16* orow = out + ((size_t)(t0 + 4 * g) * hv + h) * DV + col;   // row 4 g of the chunk
       const size_t ostride = (size_t)hv * DV;                           // elements per token
       if (n == kC) {
@@ -603,6 +657,9 @@ __global__ __launch_bounds__(kChunkWaves * 64) __attribute__((amdgpu_waves_per_e
           for (int r = 0; r < 4; ++r)
             if (16 * mt + 4 * g + r < n) orow[(16 * mt + r) * ostride] = (bf16)(scale * qs[mt][r]);
       }
+      // Stage the next chunk's Q, M and factors: every read of them for this
+      // chunk (the chain's included) happened before barrier B.
+      if (c0 + kC < len) store_out();
     }
   }
 
