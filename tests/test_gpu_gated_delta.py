@@ -46,6 +46,12 @@ CASES = {
     "recurrent_d64": ([7, 12, 3], 1, 1, 64, 64, False, None),
     "chunked_loose_bound": ([1, 16, 5, 0, 9, 16], 2, 4, 128, 128, True, 300),
     "all_empty": ([0, 0, 0], 1, 2, 64, 128, True, None),
+    "gva4": ([150, 70], 2, 8, 128, 128, True, None),
+    "single_head": ([300], 1, 1, 128, 64, True, None),
+    # 100 sequences of 1..80 tokens: many partial chunks, grid sizes not divisible by 8
+    "many_short": ([int(x) for x in np.random.default_rng(97).integers(1, 81, 100)], 2, 4, 64, 64, False, None),
+    # one serving decode step: 128 sequences of one token each from their states
+    "decode_step": ([1] * 128, 4, 8, 128, 128, True, None),
 }
 
 
