@@ -219,7 +219,8 @@ def gated_delta_case(vfa, torch, lengths, reps=5, warmup=1):
     flops = 7.0 * 128 * 128 * 32 * tokens
     res = {"ms_median": round(t, 4), "ms_p10": round(sorted(ms)[len(ms) // 10], 4),
            "ms_p90": round(sorted(ms)[(9 * len(ms)) // 10], 4), "gflop": round(flops / 1e9, 2),
-           "tflops": round(flops / t / 1e9, 2), "frac_fp32_vector_peak": round(flops / t / 1e9 / PEAK_FP32_VECTOR_TFLOPS, 4),
+           "tflops": round(flops / t / 1e9, 2),
+           "frac_fp32_vector_peak": round(flops / t / 1e9 / PEAK_FP32_VECTOR_TFLOPS, 4),
            "tokens": tokens, "longest_sequence": int(p.lengths.max())}
     del q, k, v, g, beta, cu, out
     torch.cuda.empty_cache()

@@ -110,8 +110,8 @@ def test_gated_delta_gate_extremes(name):
             idx = np.concatenate([np.arange(p.cu_seqlens[b], p.cu_seqlens[b + 1]) for b in keep])
             ii = torch.from_numpy(idx).cuda()
             cu = torch.from_numpy(np.r_[0, np.cumsum([lens[b] for b in keep])].astype(np.int32)).cuda()
-            out, fin = vfa.gated_delta_rule_fwd(x["q"][ii].contiguous(), x["k"][ii].contiguous(), x["v"][ii].contiguous(),
-                                                x["g"][ii].contiguous(), x["beta"][ii].contiguous(), cu, 16,
+            sub = {name: x[name][ii].contiguous() for name in ("q", "k", "v", "g", "beta")}
+            out, fin = vfa.gated_delta_rule_fwd(sub["q"], sub["k"], sub["v"], sub["g"], sub["beta"], cu, 16,
                                                 scale=p.scale, initial_state=torch.from_numpy(s0[keep]).cuda(),
                                                 output_final_state=True)
             want_o, want_f = o_ref[idx], f_ref[keep]

@@ -8,9 +8,11 @@
 //   o_t = scale * S^T q_t
 // with query / key head h / (Hv / Hqk). States never cross sequences.
 //
-// This kernel runs the recurrence itself in fp32: the tokens of a sequence
-// are sequential, so the parallelism is across (sequence, head, state
-// column). A column j of S belongs to 8 consecutive lanes, each holding Dk / 8
+// This kernel runs the recurrence itself in fp32, token by token; it serves
+// calls whose sequences are at most 16 tokens long (decode steps, speculative
+// tokens), where it needs no workspace and one launch. Longer sequences take
+// the chunked form (gated_delta_chunk.hip). The tokens of a sequence are
+// sequential, so the parallelism is across (sequence, head, state column). A column j of S belongs to 8 consecutive lanes, each holding Dk / 8
 // of its rows in registers, so a token's dependency chain (S^T k, then the
 // write) is Dk / 8 deep per lane; the two dot products per token (S^T k and
 // S^T q) finish with three DPP exchanges inside the 8 lanes. A workgroup

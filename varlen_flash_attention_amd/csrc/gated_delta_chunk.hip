@@ -13,7 +13,7 @@
 //
 // Two kernels:
 //   gdn_prep_kernel  one wave per (sequence, chunk, value head), all in
-//                    parallel: gamma (fp64 scan), K K^T and Q K^T on MFMA,
+//                    parallel: gamma (fp64 scan), K K^T and K Q^T on MFMA,
 //                    T = (I + A)^-1 by forward substitution in fp32, then T and
 //                    M as bf16 hi / lo pairs and the two decay factors per token
 //                    into the workspace.
@@ -85,11 +85,10 @@ __device__ __forceinline__ size_t ws_row(size_t t, int hv, int h) { return (t * 
 // ---------------------------------------------------------------------------
 // Phase 1: per (sequence, chunk, value head), independent of the state.
 template <int DK>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void gdn_prep_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
-                                                      const float* __restrict__ g, const float* __restrict__ beta,
-                                                      const int32_t* __restrict__ cu, int hqk, int hv, int n_chunks,
-                                                      bf16* __restrict__ wt, bf16* __restrict__ wm,
-                                                      float* __restrict__ we) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void gdn_prep_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const float* __restrict__ g,
+    const float* __restrict__ beta, const int32_t* __restrict__ cu, int hqk, int hv, int n_chunks,
+    bf16* __restrict__ wt, bf16* __restrict__ wm, float* __restrict__ we) {
   __shared__ __attribute__((aligned(16))) double sgam[kC];
   __shared__ float sbeta[kC];
   __shared__ __attribute__((aligned(16))) float sat[kC][kC + 4];   // A transposed: sat[j][i] = A_ij
@@ -700,7 +699,8 @@ int launch_gated_delta_chunked(const GatedDeltaArgs& a, int max_seqlen, void* wo
   bf16* wt = (bf16*)ws;
   bf16* wm = wt + rows;
   float* we = (float*)(wm + rows);
-  if (a.dk == 128) return a.dv == 128 ? launch_t<128, 128>(a, n_chunks, wt, wm, we) : launch_t<128, 64>(a, n_chunks, wt, wm, we);
+  if (a.dk == 128)
+    return a.dv == 128 ? launch_t<128, 128>(a, n_chunks, wt, wm, we) : launch_t<128, 64>(a, n_chunks, wt, wm, we);
   return a.dv == 128 ? launch_t<64, 128>(a, n_chunks, wt, wm, we) : launch_t<64, 64>(a, n_chunks, wt, wm, we);
 }
 
