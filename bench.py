@@ -13,7 +13,8 @@ Extra fields (not the headline): the embedding-style prefill with the
 last-token gather, the same long prefill without masking, decode against
 long KV sets (contiguous, and paged with 16- and 128-key pages), the q/k
 RMSNorm + rotary prologue on the long-prefill tokens, the gated delta rule
-(linear attention) on the same lengths, and the attn_update merge of the
+(linear attention) on the same lengths and one decode step of it (64
+sequences of one token, state traffic in TB/s), and the attn_update merge of the
 chunked-context config (sp=8, bsh=2048, hd=128, fp32) timed with caches
 flushed before every rep.
 
@@ -227,6 +228,39 @@ def gated_delta_case(vfa, torch, lengths, reps=5, warmup=1):
     return res
 
 
+def gated_delta_decode_case(vfa, torch, reps=50, warmup=5):
+    """One decode step of the gated delta rule: 64 sequences of one token, 16 q/k and 32 v heads, D 128,
+    from given fp32 states to new ones (the token-by-token path). Algorithmic bytes: the states read and
+    written, 2 * 64 * 32 * 128 * 128 * 4 = 268 MB (q, k, v, g, beta and the output add 0.6 MB)."""
+    import numpy as np
+    from varlen_flash_attention_amd.workloads import bf16_bits, make_gated_delta
+
+    b, hqk, hv, d = 64, 16, 32, 128
+    p = make_gated_delta([1] * b, hqk, hv, d, d, seed=94)
+
+    def dev(x):
+        return torch.from_numpy(bf16_bits(x).view(np.int16)).cuda().view(torch.bfloat16)
+
+    q, k, v = dev(p.q), dev(p.k), dev(p.v)
+    g, beta = torch.from_numpy(p.g).cuda(), torch.from_numpy(p.beta).cuda()
+    cu = torch.from_numpy(p.cu_seqlens).cuda()
+    s0 = torch.from_numpy(np.random.default_rng(95).standard_normal((b, hv, d, d)).astype(np.float32)).cuda()
+    out = torch.empty((b, hv, d), dtype=torch.bfloat16, device="cuda")
+
+    def call():
+        vfa.gated_delta_rule_fwd(q, k, v, g, beta, cu, 1, scale=p.scale, initial_state=s0,
+                                 output_final_state=True, out=out)
+
+    ms = time_calls(call, reps, warmup, torch)
+    t = median(ms)
+    nbytes = 2 * b * hv * d * d * 4
+    res = {"ms_median": round(t, 4), "state_gb": round(nbytes / 1e9, 3), "tb_per_s": round(nbytes / t / 1e9, 3),
+           "frac_hbm": round(nbytes / t / 1e6 / PEAK_HBM_GBPS, 4)}
+    del q, k, v, g, beta, cu, s0, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def merge_case(vfa, torch, reps=100, warmup=5):
     """attn_update on the chunked-context merge shape, partials from the decode workload's chunks."""
     import numpy as np
@@ -420,6 +454,8 @@ def main() -> int:
         extra["qk_norm_rope"] = prologue_case(vfa, torch, w.lengths_q)
         log("[bench] extra: gated delta rule (linear attention)")
         extra["gated_delta_rule"] = gated_delta_case(vfa, torch, w.lengths_q)
+        log("[bench] extra: gated delta rule decode step")
+        extra["gated_delta_decode_step"] = gated_delta_decode_case(vfa, torch)
         log("[bench] extra: attn_update merge")
         extra["attn_update_merge"] = merge_case(vfa, torch)
 

@@ -298,9 +298,11 @@ int32_t qk_norm_rope(const void* q_in, const void* k_in, int32_t dtype,
  *               up to 16, a token-by-token fp32 recurrence that needs no
  *               workspace; above, the chunked form (64-token chunks, two
  *               kernels) whose per-chunk matrices go to the workspace.
- * initial_state [batch, num_heads_v, head_dim_k, head_dim_v] fp32, or NULL
+ * initial_state [batch, num_heads_v, head_dim_k, head_dim_v] fp32, or NULL;
+ *               16-byte aligned (else VFA_ERR_UNSUPPORTED)
  * out           [total_tokens, num_heads_v, head_dim_v]    bf16
- * final_state   [batch, num_heads_v, head_dim_k, head_dim_v] fp32, or NULL
+ * final_state   [batch, num_heads_v, head_dim_k, head_dim_v] fp32, or NULL;
+ *               16-byte aligned (else VFA_ERR_UNSUPPORTED)
  * workspace     device memory of at least
  *               gated_delta_rule_fwd_workspace_size(total_tokens,
  *               num_heads_v, max_seqlen) bytes, 16-byte aligned, owned by

@@ -293,6 +293,8 @@ def _gdn(lib, **kw):
     (dict(ms=100), WS),                              # chunked path without a workspace
     (dict(ms=100, ws=P, wsb=16 * 32 * 520 - 1), WS),
     (dict(ms=100, ws=P, wsb=16 * 32 * 520, dv=32), UNSUP),
+    (dict(s0=P + 4), UNSUP),                         # states move in 16-byte pieces
+    (dict(s1=P + 8), UNSUP),
 ])
 def test_gated_delta_validation(lib, kw, code):
     assert _gdn(lib, **kw) == code
