@@ -374,7 +374,9 @@ attn_fwd_bf16_kernel(
       // Masked tiles: sub-blocks wholly past the block's last visible key hold
       // nothing for any row (n_sub_vis is uniform over the workgroup).
       if (decltype(masked)::value && SUBS * j + sb >= n_sub_vis) break;
-      qk(SUBS * j + sb + 1, s_next);   // the last one of the last tile reads a stale slot: computed, never used
+      // The QK after the block's last visible sub-block would never be used
+      // (masked tiles only: in full tiles it is the next sub-block's).
+      if (!decltype(masked)::value || SUBS * j + sb + 1 < n_sub_vis) qk(SUBS * j + sb + 1, s_next);
       softmax_pv(masked, s_cur, j, sb);
 #pragma unroll
       for (int qb = 0; qb < NQ; ++qb) s_cur[qb] = s_next[qb];
