@@ -311,10 +311,12 @@ int32_t qk_norm_rope(const void* q_in, const void* k_in, int32_t dtype,
  * Both paths keep the state in fp32 and round out once to bf16.
  * Supported: dtype VFA_BF16; head_dim_k and head_dim_v in {64, 128};
  * num_heads_v a multiple of num_heads_qk; scale finite.
+ * q, k, v and out must be 16-byte aligned (else VFA_ERR_UNSUPPORTED).
  * q, k, v, g, beta and out may be NULL when total_tokens == 0; the final
  * state (the initial state, or zeros) is still written.
- * Errors: VFA_ERR_WORKSPACE if the workspace is NULL or smaller than the
- * query (nothing is launched). batch == 0 returns VFA_OK.
+ * Errors: VFA_ERR_WORKSPACE if the workspace is NULL, smaller than the
+ * query or not 16-byte aligned (nothing is launched). batch == 0 returns
+ * VFA_OK.
  */
 int64_t gated_delta_rule_fwd_workspace_size(int32_t total_tokens, int32_t num_heads_v, int32_t max_seqlen);
 

@@ -295,6 +295,10 @@ def _gdn(lib, **kw):
     (dict(ms=100, ws=P, wsb=16 * 32 * 520, dv=32), UNSUP),
     (dict(s0=P + 4), UNSUP),                         # states move in 16-byte pieces
     (dict(s1=P + 8), UNSUP),
+    (dict(q=P + 2), UNSUP),                          # so do token rows
+    (dict(v=P + 8), UNSUP),
+    (dict(out=P + 4), UNSUP),
+    (dict(ms=100, ws=P + 8, wsb=16 * 32 * 520 + 8), WS),   # and the workspace
 ])
 def test_gated_delta_validation(lib, kw, code):
     assert _gdn(lib, **kw) == code

@@ -321,10 +321,11 @@ VFA_API int32_t gated_delta_rule_fwd(const void* q, const void* k, const void* v
   if (head_dim_k != 64 && head_dim_k != 128) return VFA_ERR_UNSUPPORTED;
   if (head_dim_v != 64 && head_dim_v != 128) return VFA_ERR_UNSUPPORTED;
   if (!std::isfinite(scale)) return VFA_ERR_UNSUPPORTED;
-  // States move in 16-byte pieces.
+  // Token rows, states and the workspace move in 16-byte pieces.
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return VFA_ERR_UNSUPPORTED;
   if (!aligned16(initial_state) || !aligned16(final_state)) return VFA_ERR_UNSUPPORTED;
   const int64_t need = gated_delta_rule_fwd_workspace_size(total_tokens, num_heads_v, max_seqlen);
-  if (need > 0 && (!workspace || workspace_bytes < need)) return VFA_ERR_WORKSPACE;
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace))) return VFA_ERR_WORKSPACE;
   if (debug_checks()) {
     const int r = vfa::check_cu_seqlens(cu_seqlens, total_tokens, max_seqlen, nullptr, 0, 0, batch, stream);
     if (r < 0) return VFA_ERR_LAUNCH;
