@@ -108,29 +108,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   const int lane = threadIdx.x;
   const int l32 = lane & 31, half = lane >> 5;
 
-  // gamma: inclusive prefix sum of g over the chunk, in fp64 so that the
-  // differences gamma_i - gamma_j keep fp32 accuracy however long the decay
-  // runs; each difference is then rounded to fp32 and exponentiated there.
-  double gl = lane < n ? (double)g[(size_t)(t0 + lane) * hv + h] : 0.0;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const double o = __shfl_up(gl, off, 64);
-    if (lane >= off) gl += o;
-  }
-  sgam[lane] = gl;                              // lanes past n repeat gamma_{n-1}
-  sbeta[lane] = lane < n ? beta[(size_t)(t0 + lane) * hv + h] : 0.f;
-  __syncthreads();
-  if (lane < n) {
-    const size_t o = (size_t)(t0 + lane) * hv + h;
-    we[2 * o] = decay_factor(gl);                     // e^gamma_i
-    we[2 * o + 1] = decay_factor(sgam[n - 1] - gl);   // e^(gamma_end - gamma_i)
-  }
-
-  // Products with rows m = key token j and columns n = token i, so that a
-  // lane (column i) holds four consecutive j of row i of A and M: K K^T (for
-  // A) and K Q^T (for M). Tiles (mt, nt) = (0,0), (0,1), (1,1); tile (1, 0)
-  // has j > i only, where both are zero. All operand loads are issued before
-  // the first product.
+  // g and beta first (rows past n repeat the last token, then are zeroed),
+  // then the K and Q operands of the products below (rows m = key token j,
+  // columns n = token i, same clamp): the scan waits only for the first two,
+  // and the operands arrive while it runs.
+  const size_t gb_row = (size_t)(t0 + min(lane, n - 1)) * hv + h;
+  const float g_raw = g[gb_row];
+  const float b_raw = beta[gb_row];
   bf16x8 ka[2][DK / 16], qa[2][DK / 16];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
@@ -141,6 +125,29 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       qa[t][ks] = *(const bf16x8*)(q + row + 16 * ks);
     }
   }
+
+  // gamma: inclusive prefix sum of g over the chunk, in fp64 so that the
+  // differences gamma_i - gamma_j keep fp32 accuracy however long the decay
+  // runs; each difference is then rounded to fp32 and exponentiated there.
+  double gl = lane < n ? (double)g_raw : 0.0;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const double o = __shfl_up(gl, off, 64);
+    if (lane >= off) gl += o;
+  }
+  sgam[lane] = gl;                              // lanes past n repeat gamma_{n-1}
+  sbeta[lane] = lane < n ? b_raw : 0.f;
+  __syncthreads();
+  if (lane < n) {
+    const size_t o = (size_t)(t0 + lane) * hv + h;
+    we[2 * o] = decay_factor(gl);                     // e^gamma_i
+    we[2 * o + 1] = decay_factor(sgam[n - 1] - gl);   // e^(gamma_end - gamma_i)
+  }
+
+  // Products with rows m = key token j and columns n = token i, so that a
+  // lane (column i) holds four consecutive j of row i of A and M: K K^T (for
+  // A) and K Q^T (for M). Tiles (mt, nt) = (0,0), (0,1), (1,1); tile (1, 0)
+  // has j > i only, where both are zero.
   // Every operand is consumed here, so all loads are in flight together and
   // the products below wait on memory once (left alone, the compiler keeps
   // only a few loads ahead of the products and pays several round trips).
@@ -158,16 +165,45 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       kq[tile] = mfma(ka[kMt[tile]][ks], qa[kNt[tile]][ks], kq[tile]);
     }
 
-  // A_ij = beta_i e^(gamma_i - gamma_j) k_i.k_j (j < i) into LDS as sat[j][i];
-  // M_ij = e^(gamma_i - gamma_j) q_i.k_j (j <= i), hi / lo, four consecutive
-  // columns per 8-byte store into the workspace.
+  // The workspace rows of T and M (256 bytes each, 8 KB apart from token to
+  // token) leave through LDS: each matrix is first laid out there by rows
+  // (272-byte stride), then written as whole rows, 16 bytes per lane. Stored
+  // straight from registers they take 2- or 8-byte pieces of many rows per
+  // instruction. The staging reuses the array that holds A.
+  constexpr int SROW = 2 * kC * 2 + 16;
+  static_assert(kC * SROW <= (int)sizeof(sat), "staging must fit the A array");
+  char VFA_LDS* stg = (char VFA_LDS*)&sat[0][0];
+  // Lane l moves 16-byte piece l % 16 of rows l / 16 + 4 it. All pieces are
+  // read before the first store, and full chunks store without a row test
+  // (a per-row branch makes the compiler pair each read with its store).
+  auto store_rows = [&](bf16* base) __attribute__((always_inline)) {
+    constexpr int NP = kC * 16 / 64;
+    const int r0 = lane >> 4, c16 = lane & 15;
+    u32x4 val[NP];
+#pragma unroll
+    for (int it = 0; it < NP; ++it) val[it] = *(const u32x4 VFA_LDS*)(stg + (r0 + 4 * it) * SROW + 16 * c16);
+    bf16* dst = base + ws_row(t0 + r0, hv, h) + 8 * c16;
+    const size_t step = (size_t)4 * hv * (2 * kC);      // 4 rows further
+    if (n == kC) {
+#pragma unroll
+      for (int it = 0; it < NP; ++it) *(u32x4*)(dst + it * step) = val[it];
+    } else {
+#pragma unroll
+      for (int it = 0; it < NP; ++it)
+        if (r0 + 4 * it < n) *(u32x4*)(dst + it * step) = val[it];
+    }
+  };
+
+  // A_ij = beta_i e^(gamma_i - gamma_j) k_i.k_j (j < i), kept in registers
+  // until M has left; M_ij = e^(gamma_i - gamma_j) q_i.k_j (j <= i), hi / lo,
+  // four consecutive columns per 8-byte write into the staging rows.
+  float av[3][16];
 #pragma unroll
   for (int tile = 0; tile < 3; ++tile) {
     const int i = 32 * kNt[tile] + l32;
     const double gi = sgam[i];
     const float bi = sbeta[i];
     const bool live = i < n;
-    bf16* mrow = wm + ws_row(t0 + min(i, n - 1), hv, h);
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       const int jb = 32 * kMt[tile] + 8 * g4 + 4 * half;
@@ -183,52 +219,66 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         // which the select drops): no branch around the fp64 difference.
         const float e = decay_factor(gi - gj[z]);
         const float d = (j <= i) ? e : 0.f;
-        sat[j][i] = (live && j < i) ? bi * d * kk[tile][r] : 0.f;
+        av[tile][r] = (live && j < i) ? bi * d * kk[tile][r] : 0.f;
         mv[z] = d * kq[tile][r];
       }
       const bf16x2 h01 = f32x2_to_bf16x2(mv[0], mv[1]), h23 = f32x2_to_bf16x2(mv[2], mv[3]);
       const bf16x2 l01 = f32x2_to_bf16x2(mv[0] - (float)h01[0], mv[1] - (float)h01[1]);
       const bf16x2 l23 = f32x2_to_bf16x2(mv[2] - (float)h23[0], mv[3] - (float)h23[1]);
-      if (live) {
-        const int j0 = 32 * kMt[tile] + 8 * g4 + 4 * half;
-        *(bf16x4*)(mrow + j0) = bf16x4{h01[0], h01[1], h23[0], h23[1]};
-        *(bf16x4*)(mrow + kC + j0) = bf16x4{l01[0], l01[1], l23[0], l23[1]};
-      }
+      char VFA_LDS* mrow = stg + i * SROW + 2 * jb;
+      *(bf16x4 VFA_LDS*)mrow = bf16x4{h01[0], h01[1], h23[0], h23[1]};
+      *(bf16x4 VFA_LDS*)(mrow + 2 * kC) = bf16x4{l01[0], l01[1], l23[0], l23[1]};
     }
   }
   // Tile (1, 0): j >= 32 > i, zero in A and M.
-  {
-    const int i = l32;
-    bf16* mrow = wm + ws_row(t0 + min(i, n - 1), hv, h);
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const int j0 = 32 + 8 * g4 + 4 * half;
-#pragma unroll
-      for (int z = 0; z < 4; ++z) sat[j0 + z][i] = 0.f;
-      if (i < n) {
-        *(bf16x4*)(mrow + j0) = bf16x4{};
-        *(bf16x4*)(mrow + kC + j0) = bf16x4{};
-      }
-    }
+  for (int g4 = 0; g4 < 4; ++g4) {
+    char VFA_LDS* mrow = stg + l32 * SROW + 2 * (32 + 8 * g4 + 4 * half);
+    *(bf16x4 VFA_LDS*)mrow = bf16x4{};
+    *(bf16x4 VFA_LDS*)(mrow + 2 * kC) = bf16x4{};
   }
+  __syncthreads();
+  store_rows(wm);
+  __syncthreads();
+  // A into the same array, transposed: sat[j][i] = A_ij.
+#pragma unroll
+  for (int tile = 0; tile < 3; ++tile) {
+    const int i = 32 * kNt[tile] + l32;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sat[32 * kMt[tile] + 8 * (r / 4) + 4 * half + r % 4][i] = av[tile][r];
+  }
+#pragma unroll
+  for (int g4 = 0; g4 < 4; ++g4)
+#pragma unroll
+    for (int z = 0; z < 4; ++z) sat[32 + 8 * g4 + 4 * half + z][l32] = 0.f;
   __syncthreads();
 
   // T = (I + A)^-1 by forward substitution, lane = column c of T, in the
   // right-looking order: x starts as e_c; once x_j is final, every later row
   // takes its term, x_i -= A_ij x_j (i > j). The updates of one step are
   // independent, and column j of A is one broadcast read per four rows.
+  // Column j + 1 of A is read while step j's updates run (read just before
+  // its use, each broadcast read waits out a full LDS round trip).
   float x[kC];
 #pragma unroll
   for (int i = 0; i < kC; ++i) x[i] = (i == lane) ? 1.f : 0.f;
+  f32x4 acol[2][kC / 4];
+#pragma unroll
+  for (int q4 = 0; q4 < kC / 4; ++q4) acol[0][q4] = *(const f32x4*)&sat[0][4 * q4];
 #pragma unroll
   for (int j = 0; j < kC - 1; ++j) {
+    const int cur = j & 1;
+    if (j + 1 < kC - 1) {
+#pragma unroll
+      for (int q4 = (j + 2) >> 2; q4 < kC / 4; ++q4) acol[cur ^ 1][q4] = *(const f32x4*)&sat[j + 1][4 * q4];
+    }
+    __builtin_amdgcn_sched_barrier(0);
     const float xj = x[j];
 #pragma unroll
-    for (int i4 = (j + 1) & ~3; i4 < kC; i4 += 4) {
-      const f32x4 a = *(const f32x4*)&sat[j][i4];
+    for (int q4 = (j + 1) >> 2; q4 < kC / 4; ++q4) {
 #pragma unroll
       for (int z = 0; z < 4; ++z)
-        if (i4 + z > j) x[i4 + z] -= a[z] * xj;
+        if (4 * q4 + z > j) x[4 * q4 + z] -= acol[cur][q4][z] * xj;
     }
     // Materialise this step's updates here. Left free, the compiler defers
     // each row's chain of updates to its end, keeping every loaded A value
@@ -236,17 +286,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 #pragma unroll
     for (int i = j + 1; i < kC; ++i) __asm__ volatile("" : "+v"(x[i]));
   }
-  bf16* trow = wt + ws_row(t0, hv, h) + lane;       // row i of T is hv * 2kC elements further per token
-  const size_t tstride = (size_t)hv * 2 * kC;
+  __syncthreads();
+  // T rows (hi then lo) through the staging rows: lane c holds column c.
 #pragma unroll
   for (int i = 0; i < kC; ++i) {
-    if (i < n) {
-      const bf16 th = (bf16)x[i];
-      trow[0] = th;
-      trow[kC] = (bf16)(x[i] - (float)th);
-    }
-    trow += tstride;
+    const bf16 th = (bf16)x[i];
+    *(bf16 VFA_LDS*)(stg + i * SROW + 2 * lane) = th;
+    *(bf16 VFA_LDS*)(stg + i * SROW + 2 * kC + 2 * lane) = (bf16)(x[i] - (float)th);
   }
+  __syncthreads();
+  store_rows(wt);
 }
 
 // ---------------------------------------------------------------------------
