@@ -291,14 +291,14 @@ def _gdn(lib, **kw):
     (dict(scale=float("inf")), UNSUP),
     (dict(ms=-1), SHAPE),
     (dict(ms=100), WS),                              # chunked path without a workspace
-    (dict(ms=100, ws=P, wsb=16 * 32 * 520 - 1), WS),
-    (dict(ms=100, ws=P, wsb=16 * 32 * 520, dv=32), UNSUP),
+    (dict(ms=100, ws=P, wsb=16 * 32 * 520 + 16384 - 1), WS),
+    (dict(ms=100, ws=P, wsb=16 * 32 * 520 + 16384, dv=32), UNSUP),
     (dict(s0=P + 4), UNSUP),                         # states move in 16-byte pieces
     (dict(s1=P + 8), UNSUP),
     (dict(q=P + 2), UNSUP),                          # so do token rows
     (dict(v=P + 8), UNSUP),
     (dict(out=P + 4), UNSUP),
-    (dict(ms=100, ws=P + 8, wsb=16 * 32 * 520 + 8), WS),   # and the workspace
+    (dict(ms=100, ws=P + 8, wsb=16 * 32 * 520 + 16384 + 8), WS),   # and the workspace
 ])
 def test_gated_delta_validation(lib, kw, code):
     assert _gdn(lib, **kw) == code
@@ -306,9 +306,10 @@ def test_gated_delta_validation(lib, kw, code):
 
 def test_gated_delta_workspace_size(lib):
     """Lengths up to 16 take the recurrence (no workspace); above, the chunked form keeps two 64-wide
-    bf16 hi / lo rows (T and M) and two fp32 decay factors per (token, value head): 520 bytes."""
+    bf16 hi / lo rows (T and M) and two fp32 decay factors per (token, value head): 520 bytes; plus a
+    fixed 16 KiB slot for the order in which the chunk kernel takes the sequences (up to 4096 ranked)."""
     ws = lib.gated_delta_rule_fwd_workspace_size
     assert ws(35324, 32, 16) == 0
-    assert ws(35324, 32, 17) == 35324 * 32 * 520
+    assert ws(35324, 32, 17) == 35324 * 32 * 520 + 16384
     assert ws(0, 32, 8192) == 0
-    assert ws(1, 1, 8192) == 520
+    assert ws(1, 1, 8192) == 520 + 16384

@@ -16,11 +16,15 @@
 //                    parallel: gamma (fp64 scan), K K^T and K Q^T on MFMA,
 //                    T = (I + A)^-1 by forward substitution in fp32, then T and
 //                    M as bf16 hi / lo pairs and the two decay factors per token
-//                    into the workspace.
+//                    into the workspace. Its first workgroups also rank the
+//                    sequences by length (longest first) for the second kernel.
 //   gdn_chunk_kernel one workgroup per (sequence, value head, 64 state
 //                    columns), one wave per 16 columns, chunks in order: y = K S and Q S, then
 //                    U = T r with r = beta (V - e^gamma y), then M U for the
-//                    output and K^T U~ for the state.
+//                    output and K^T U~ for the state. Workgroups take the
+//                    sequences longest first: each one's chunks form a serial
+//                    chain, and a long chain started late ends after the rest
+//                    of the grid has drained.
 //
 // Precision: the state stays fp32 in MFMA accumulators. Products with an fp32
 // operand split it into bf16 hi + lo and take hi.hi + hi.lo + lo.hi (K and Q
@@ -79,7 +83,8 @@ __device__ __forceinline__ void xcd_decode(int idx, int items, int inner, int& i
 __device__ __forceinline__ float decay_factor(double x) { return fast_exp2((float)x * kLog2e); }
 
 // Workspace rows, one per (token, value head): T (hi then lo, kC each) and M
-// (the same), bf16; then two fp32 decay factors per (token, value head).
+// (the same), bf16; then two fp32 decay factors per (token, value head); then
+// the chunk kernel's sequence order (a fixed slot of kOrderMax int32).
 __device__ __forceinline__ size_t ws_row(size_t t, int hv, int h) { return (t * hv + h) * (2 * kC); }
 
 // ---------------------------------------------------------------------------
@@ -87,8 +92,23 @@ __device__ __forceinline__ size_t ws_row(size_t t, int hv, int h) { return (t * 
 template <int DK>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void gdn_prep_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const float* __restrict__ g,
-    const float* __restrict__ beta, const int32_t* __restrict__ cu, int hqk, int hv, int n_chunks,
-    bf16* __restrict__ wt, bf16* __restrict__ wm, float* __restrict__ we) {
+    const float* __restrict__ beta, const int32_t* __restrict__ cu, int batch, int hqk, int hv, int n_chunks,
+    bf16* __restrict__ wt, bf16* __restrict__ wm, float* __restrict__ we, int32_t* __restrict__ order) {
+  // Sequence order for the chunk kernel: order[r] = the sequence of rank r by
+  // length, longest first, ties by index (a permutation). One sequence per
+  // lane of the first ceil(batch / 64) workgroups, ranked against all others.
+  if (order && (int)blockIdx.x * 64 < batch) {
+    const int sq = (int)blockIdx.x * 64 + (int)threadIdx.x;
+    if (sq < batch) {
+      const int ls = cu[sq + 1] - cu[sq];
+      int rank = 0;
+      for (int b2 = 0; b2 < batch; ++b2) {
+        const int l2 = cu[b2 + 1] - cu[b2];
+        rank += (l2 > ls) || (l2 == ls && b2 < sq);
+      }
+      order[rank] = sq;
+    }
+  }
   __shared__ __attribute__((aligned(16))) double sgam[kC];
   __shared__ float sbeta[kC];
   __shared__ __attribute__((aligned(16))) float sat[kC][kC + 4];   // A transposed: sat[j][i] = A_ij
@@ -384,7 +404,8 @@ __global__ __launch_bounds__(kChunkWaves * 64) __attribute__((amdgpu_waves_per_e
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ beta, const int32_t* __restrict__ cu, int hqk, int hv, float scale,
     const float* __restrict__ s_init, bf16* __restrict__ out, float* __restrict__ s_final,
-    const bf16* __restrict__ wt, const bf16* __restrict__ wm, const float* __restrict__ we) {
+    const bf16* __restrict__ wt, const bf16* __restrict__ wm, const float* __restrict__ we,
+    const int32_t* __restrict__ order) {
   using S = ChunkSmem<DK>;
   constexpr int NCG = DV / kGroupCols;  // column groups per head
   constexpr int NDT = DK / 16;          // 16-row tiles of the state
@@ -400,7 +421,7 @@ __global__ __launch_bounds__(kChunkWaves * 64) __attribute__((amdgpu_waves_per_e
   int item, cg;
   xcd_decode(blockIdx.x, gridDim.x / NCG, NCG, item, cg);
   const int h = item % hv;
-  const int b = item / hv;
+  const int b = order ? order[item / hv] : item / hv;   // longest sequences first
   const int hk = h / (hv / hqk);
   const int ts = cu[b];
   const int len = cu[b + 1] - ts;
@@ -720,24 +741,29 @@ __global__ __launch_bounds__(kChunkWaves * 64) __attribute__((amdgpu_waves_per_e
 }
 
 template <int DK, int DV>
-int launch_t(const GatedDeltaArgs& a, int n_chunks, bf16* wt, bf16* wm, float* we) {
+int launch_t(const GatedDeltaArgs& a, int n_chunks, bf16* wt, bf16* wm, float* we, int32_t* order) {
   const long long prep = (long long)a.batch * a.hv * n_chunks;
   const long long main_blocks = (long long)a.batch * a.hv * (DV / kGroupCols);
   if (prep > 0x7fffffffLL || main_blocks > 0x7fffffffLL) return -1;
   hipStream_t s = (hipStream_t)a.stream;
   hipLaunchKernelGGL((gdn_prep_kernel<DK>), dim3((unsigned)prep), dim3(64), 0, s, (const bf16*)a.q,
-                     (const bf16*)a.k, a.g, a.beta, a.cu, a.hqk, a.hv, n_chunks, wt, wm, we);
+                     (const bf16*)a.k, a.g, a.beta, a.cu, a.batch, a.hqk, a.hv, n_chunks, wt, wm, we, order);
   if (hipGetLastError() != hipSuccess) return -1;
   hipLaunchKernelGGL((gdn_chunk_kernel<DK, DV>), dim3((unsigned)main_blocks), dim3(kChunkWaves * 64), 0, s,
                      (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.beta, a.cu, a.hqk, a.hv, a.scale,
-                     a.s_init, (bf16*)a.out, a.s_final, (const bf16*)wt, (const bf16*)wm, (const float*)we);
+                     a.s_init, (bf16*)a.out, a.s_final, (const bf16*)wt, (const bf16*)wm, (const float*)we,
+                     (const int32_t*)order);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 }  // namespace
 
+// Up to this many sequences are ranked by length for the chunk kernel; larger
+// batches keep their own order. The ranking costs O(batch) per sequence.
+constexpr int kOrderMax = 4096;
+
 size_t gated_delta_chunk_workspace(long long tokens, int hv) {
-  return (size_t)tokens * hv * (2 * 2 * kC * sizeof(bf16) + 2 * sizeof(float));
+  return (size_t)tokens * hv * (2 * 2 * kC * sizeof(bf16) + 2 * sizeof(float)) + kOrderMax * sizeof(int32_t);
 }
 
 int launch_gated_delta_chunked(const GatedDeltaArgs& a, int max_seqlen, void* workspace) {
@@ -748,9 +774,12 @@ int launch_gated_delta_chunked(const GatedDeltaArgs& a, int max_seqlen, void* wo
   bf16* wt = (bf16*)ws;
   bf16* wm = wt + rows;
   float* we = (float*)(wm + rows);
+  int32_t* order = a.batch <= kOrderMax ? (int32_t*)(we + 2 * (size_t)a.tokens * a.hv) : nullptr;
   if (a.dk == 128)
-    return a.dv == 128 ? launch_t<128, 128>(a, n_chunks, wt, wm, we) : launch_t<128, 64>(a, n_chunks, wt, wm, we);
-  return a.dv == 128 ? launch_t<64, 128>(a, n_chunks, wt, wm, we) : launch_t<64, 64>(a, n_chunks, wt, wm, we);
+    return a.dv == 128 ? launch_t<128, 128>(a, n_chunks, wt, wm, we, order)
+                       : launch_t<128, 64>(a, n_chunks, wt, wm, we, order);
+  return a.dv == 128 ? launch_t<64, 128>(a, n_chunks, wt, wm, we, order)
+                     : launch_t<64, 64>(a, n_chunks, wt, wm, we, order);
 }
 
 }  // namespace vfa

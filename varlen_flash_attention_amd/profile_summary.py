@@ -117,7 +117,7 @@ def main(src, dst):
             rec = (sum(fetch[name]) / len(fetch[name]), sum(write[name]) / len(write[name]), f_b, w_b)
     tl += ["", "attn_update_kernel<float, 128, 8, 1> runs the 2048-row merge shape (cold and warm calls "
            "averaged, plus the 4x sweep point); <..., 2> the 16x and 64x sweep points (two rows per thread).",
-           "gdn_prep_kernel writes the per-chunk T and M rows and decay factors (520 B per token and value head); "
+           "gdn_prep_kernel writes the per-chunk T and M rows and decay factors (520 B per token and value head) and ranks the sequences by length; "
            "gdn_chunk_kernel reads them back with the chunk's K, Q and V and writes the output."]
     open(os.path.join(dst, "bench_kernels.hbm_traffic.txt"), "w").write("\n".join(tl) + "\n")
 
