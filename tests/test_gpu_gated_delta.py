@@ -52,6 +52,11 @@ CASES = {
     "many_short": ([int(x) for x in np.random.default_rng(97).integers(1, 81, 100)], 2, 4, 64, 64, False, None),
     # one serving decode step: 128 sequences of one token each from their states
     "decode_step": ([1] * 128, 4, 8, 128, 128, True, None),
+    # the chunked path ranks up to 4096 sequences by length (ties by index) for its second kernel and
+    # keeps larger batches in index order: both sides of that limit, lengths 17..19 (many ties)
+    "ranked_4096": ([int(x) for x in np.random.default_rng(5).integers(17, 20, 4096)], 1, 1, 64, 64, False, None),
+    "unranked_4097": ([int(x) for x in np.random.default_rng(6).integers(17, 20, 4097)], 1, 1, 64, 64, True,
+                      None),
 }
 
 
