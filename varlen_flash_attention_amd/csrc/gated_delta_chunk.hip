@@ -564,17 +564,22 @@ __global__ __launch_bounds__(kChunkWaves * 64) __attribute__((amdgpu_waves_per_e
       __syncthreads();                  // A: chunk staged, S of this chunk start in sbuf
       if (c0 + kC < len) load_chain(c0 + kC);   // next chunk, in flight during this one
 
-      // y = K S (hi and lo); rows: chunk tokens 16 mt + 4 g + r.
+      // y = K S (hi and lo); rows: chunk tokens 16 mt + 4 g + r. All products
+      // below run k step outer, row tile inner: each step's operands are read
+      // together and the tiles' independent accumulators alternate, instead of
+      // one tile's dependent chain at a time behind one read per step (each
+      // accumulator still sums in the same order).
       f32x4 y[4] = {};
+      const char VFA_LDS* kr = sk + c16 * S::KSTR + 8 * g;
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const char VFA_LDS* kr = sk + (16 * mt + c16) * S::KSTR + 8 * g;
+      for (int ks = 0; ks < NKS; ++ks) {
+        bf16x8 ak[4];
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          const bf16x8 ak = lds_perm16(kr + 64 * ks);
-          y[mt] = mfma16(ak, sh[ks], y[mt]);
-          y[mt] = mfma16(ak, sl[ks], y[mt]);
-        }
+        for (int mt = 0; mt < 4; ++mt) ak[mt] = lds_perm16(kr + 16 * mt * S::KSTR + 64 * ks);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) y[mt] = mfma16(ak[mt], sh[ks], y[mt]);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) y[mt] = mfma16(ak[mt], sl[ks], y[mt]);
       }
       // r = beta (v - e^gamma y) in place; V comes through the transposed read,
       // already in accumulator row order.
@@ -598,16 +603,21 @@ __global__ __launch_bounds__(kChunkWaves * 64) __attribute__((amdgpu_waves_per_e
 
       // U = T r, published (hi / lo) for the output wave's M U.
       f32x4 u[4] = {};
+      const char VFA_LDS* tr = stt + c16 * S::TSTR + 8 * g;
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const char VFA_LDS* tr = stt + (16 * mt + c16) * S::TSTR + 8 * g;
+      for (int kk = 0; kk < 2; ++kk) {
+        bf16x8 th[4], tl[4];
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const bf16x8 th = lds_perm16(tr + 64 * kk), tl = lds_perm16(tr + 2 * kC + 64 * kk);
-          u[mt] = mfma16(th, rh[kk], u[mt]);
-          u[mt] = mfma16(th, rl[kk], u[mt]);
-          u[mt] = mfma16(tl, rh[kk], u[mt]);
+        for (int mt = 0; mt < 4; ++mt) {
+          th[mt] = lds_perm16(tr + 16 * mt * S::TSTR + 64 * kk);
+          tl[mt] = lds_perm16(tr + 16 * mt * S::TSTR + 2 * kC + 64 * kk);
         }
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) u[mt] = mfma16(th[mt], rh[kk], u[mt]);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) u[mt] = mfma16(th[mt], rl[kk], u[mt]);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) u[mt] = mfma16(tl[mt], rh[kk], u[mt]);
       }
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
@@ -634,15 +644,23 @@ __global__ __launch_bounds__(kChunkWaves * 64) __attribute__((amdgpu_waves_per_e
       // S <- e^gamma_end S + K^T U~ (this chunk's K buffer, which the staging
       // of the next chunk does not touch), then its split for the next chunk.
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
+      for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) st[dt][r] *= decay;
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const char VFA_LDS* p = sk + (32 * kk + tr_key) * S::KSTR + tr_d * 2 + 32 * dt;
-          const bf16x8 a = lds_read_tr(p, p + 16 * S::KSTR);
-          st[dt] = mfma16(a, wh[kk], st[dt]);
-          st[dt] = mfma16(a, wl[kk], st[dt]);
+      for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+        for (int d0 = 0; d0 < NDT; d0 += 4) {       // four row tiles per batch of reads
+          bf16x8 a[4];
+#pragma unroll
+          for (int dd = 0; dd < 4; ++dd) {
+            const char VFA_LDS* p = sk + (32 * kk + tr_key) * S::KSTR + tr_d * 2 + 32 * (d0 + dd);
+            a[dd] = lds_read_tr(p, p + 16 * S::KSTR);
+          }
+#pragma unroll
+          for (int dd = 0; dd < 4; ++dd) st[d0 + dd] = mfma16(a[dd], wh[kk], st[d0 + dd]);
+#pragma unroll
+          for (int dd = 0; dd < 4; ++dd) st[d0 + dd] = mfma16(a[dd], wl[kk], st[d0 + dd]);
         }
       }
 #pragma unroll
@@ -667,17 +685,22 @@ __global__ __launch_bounds__(kChunkWaves * 64) __attribute__((amdgpu_waves_per_e
       if (c0 + kC < len) load_out(c0 + kC);     // next chunk, in flight during this one
 
       // Q S from the chain wave's published S (hi and lo), scaled by e^gamma.
-      f32x4 qs[4];
+      f32x4 qs[4] = {};
+      const char VFA_LDS* qr = sq + c16 * S::QSTR + 8 * g;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const bf16x8 bh = *(const bf16x8 VFA_LDS*)(sbuf + (2 * ks) * 64 * 16);
+        const bf16x8 bl = *(const bf16x8 VFA_LDS*)(sbuf + (2 * ks + 1) * 64 * 16);
+        bf16x8 aq[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) aq[mt] = lds_perm16(qr + 16 * mt * S::QSTR + 64 * ks);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) qs[mt] = mfma16(aq[mt], bh, qs[mt]);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) qs[mt] = mfma16(aq[mt], bl, qs[mt]);
+      }
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        qs[mt] = f32x4{};
-        const char VFA_LDS* qr = sq + (16 * mt + c16) * S::QSTR + 8 * g;
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          const bf16x8 aq = lds_perm16(qr + 64 * ks);
-          qs[mt] = mfma16(aq, *(const bf16x8 VFA_LDS*)(sbuf + (2 * ks) * 64 * 16), qs[mt]);
-          qs[mt] = mfma16(aq, *(const bf16x8 VFA_LDS*)(sbuf + (2 * ks + 1) * 64 * 16), qs[mt]);
-        }
         const f32x4 e1 = *(const f32x4*)&se1[16 * mt + 4 * g];
 #pragma unroll
         for (int z = 0; z < 4; ++z) qs[mt][z] *= e1[z];
@@ -705,13 +728,14 @@ __global__ __launch_bounds__(kChunkWaves * 64) __attribute__((amdgpu_waves_per_e
         ul[kk] = *(const bf16x8 VFA_LDS*)(ubuf + (2 * kk + 1) * 64 * 16);
       }
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+      for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          qs[mt] = mfma16(mh[mt][kk], uh[kk], qs[mt]);
-          qs[mt] = mfma16(mh[mt][kk], ul[kk], qs[mt]);
-          qs[mt] = mfma16(ml[mt][kk], uh[kk], qs[mt]);
-        }
+        for (int mt = 0; mt < 4; ++mt) qs[mt] = mfma16(mh[mt][kk], uh[kk], qs[mt]);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) qs[mt] = mfma16(mh[mt][kk], ul[kk], qs[mt]);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) qs[mt] = mfma16(ml[mt][kk], uh[kk], qs[mt]);
+      }
       bf16* orow = out + ((size_t)(t0 + 4 * g) * hv + h) * DV + col;   // row 4 g of the chunk
       const size_t ostride = (size_t)hv * DV;                           // elements per token
       if (n == kC) {
