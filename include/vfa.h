@@ -310,7 +310,9 @@ int32_t qk_norm_rope(const void* q_in, const void* k_in, int32_t dtype,
  *               overwritten. NULL with 0 bytes when the size query returns 0.
  * Both paths keep the state in fp32 and round out once to bf16.
  * Supported: dtype VFA_BF16; head_dim_k and head_dim_v in {64, 128};
- * num_heads_v a multiple of num_heads_qk; scale finite.
+ * num_heads_v a multiple of num_heads_qk; scale finite; on the chunked
+ * path, num_heads_v * max(head_dim_v, 128) < 2^25 and num_heads_qk *
+ * head_dim_k < 2^25 (else VFA_ERR_UNSUPPORTED).
  * q, k, v and out must be 16-byte aligned (else VFA_ERR_UNSUPPORTED).
  * q, k, v, g, beta and out may be NULL when total_tokens == 0; the final
  * state (the initial state, or zeros) is still written.

@@ -299,6 +299,7 @@ def _gdn(lib, **kw):
     (dict(v=P + 8), UNSUP),
     (dict(out=P + 4), UNSUP),
     (dict(ms=100, ws=P + 8, wsb=16 * 32 * 520 + 16384 + 8), WS),   # and the workspace
+    (dict(ms=100, ws=P, wsb=1 << 60, hqk=1 << 18, hv=1 << 18), UNSUP),   # chunk spans past 32-bit offsets
 ])
 def test_gated_delta_validation(lib, kw, code):
     assert _gdn(lib, **kw) == code

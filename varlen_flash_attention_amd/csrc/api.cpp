@@ -11,6 +11,7 @@
 // attention call of "From GPU to NPU: Qwen3-Embedding on Ascend" (section 2.1
 // and core optimisation 5: head counts, TND layout, per-sequence lengths,
 // scale, causal flag).
+#include <algorithm>
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
@@ -325,6 +326,11 @@ VFA_API int32_t gated_delta_rule_fwd(const void* q, const void* k, const void* v
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return VFA_ERR_UNSUPPORTED;
   if (!aligned16(initial_state) || !aligned16(final_state)) return VFA_ERR_UNSUPPORTED;
   const int64_t need = gated_delta_rule_fwd_workspace_size(total_tokens, num_heads_v, max_seqlen);
+  // The chunked path addresses a 64-token chunk of each tensor with 32-bit offsets.
+  constexpr int64_t kChunkSpan = 64LL * 2;   // 64 tokens, bf16
+  if (need > 0 && (kChunkSpan * num_heads_qk * head_dim_k >= (1LL << 32) ||
+                   kChunkSpan * num_heads_v * std::max(head_dim_v, 128) >= (1LL << 32)))
+    return VFA_ERR_UNSUPPORTED;
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace))) return VFA_ERR_WORKSPACE;
   if (debug_checks()) {
     const int r = vfa::check_cu_seqlens(cu_seqlens, total_tokens, max_seqlen, nullptr, 0, 0, batch, stream);

@@ -470,27 +470,36 @@ __global__ __launch_bounds__(kChunkWaves * 64) __attribute__((amdgpu_waves_per_e
   u32x4 pk[S::PK], pt[S::PT], pv[S::PV];      // chain
   u32x4 pq[S::PK], pm[S::PT];                  // output
   float pe1 = 0.f, pe2 = 0.f, pbt = 0.f;      // output
+  // Piece e = stid + i STAGERS of a staged tensor is row e / PR, 16-byte
+  // column e % PR. In a full chunk its address is the chunk's first row (a
+  // wave-uniform pointer) plus a 32-bit lane offset that stays the same for
+  // every chunk (the entry point keeps 64 rows of each tensor under 4 GiB);
+  // only a sequence's last, partial chunk clamps rows to its end.
+  auto gather = [&](auto& dst, int pr, const char* base, uint32_t row_bytes, int n) __attribute__((always_inline)) {
+    constexpr int CNT = sizeof(dst) / sizeof(dst[0]);
+    if (n == kC) {
+#pragma unroll
+      for (int i = 0; i < CNT; ++i) {
+        const int e = stid + i * S::STAGERS;
+        dst[i] = *(const u32x4*)(base + ((uint32_t)(e / pr) * row_bytes + 16u * (uint32_t)(e % pr)));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < CNT; ++i) {
+        const int e = stid + i * S::STAGERS;
+        dst[i] = *(const u32x4*)(base + (size_t)min(e / pr, n - 1) * row_bytes + 16 * (e % pr));
+      }
+    }
+  };
+  const uint32_t k_row = (uint32_t)hqk * DK * sizeof(bf16);          // K and Q
+  const uint32_t w_row = (uint32_t)hv * 2 * kC * sizeof(bf16);       // T and M
+  const uint32_t v_row = (uint32_t)hv * DV * sizeof(bf16);
   auto load_chain = [&](int c0) __attribute__((always_inline)) {
     const int n = min(kC, len - c0);
     const int t0 = ts + c0;
-#pragma unroll
-    for (int i = 0; i < S::PK; ++i) {
-      const int e = stid + i * S::STAGERS;
-      const int r = min(e / (DK / 8), n - 1), c8 = e % (DK / 8);
-      pk[i] = *(const u32x4*)(k + ((size_t)(t0 + r) * hqk + hk) * DK + 8 * c8);
-    }
-#pragma unroll
-    for (int i = 0; i < S::PT; ++i) {
-      const int e = stid + i * S::STAGERS;
-      const int r = min(e / (2 * kC / 8), n - 1), c8 = e % (2 * kC / 8);
-      pt[i] = *(const u32x4*)(wt + ws_row(t0 + r, hv, h) + 8 * c8);
-    }
-#pragma unroll
-    for (int i = 0; i < S::PV; ++i) {
-      const int e = stid + i * S::STAGERS;
-      const int r = min(e / (S::DV / 8), n - 1), c8 = e % (S::DV / 8);
-      pv[i] = *(const u32x4*)(v + ((size_t)(t0 + r) * hv + h) * DV + cg * kGroupCols + 8 * c8);
-    }
+    gather(pk, DK / 8, (const char*)(k + ((size_t)t0 * hqk + hk) * DK), k_row, n);
+    gather(pt, 2 * kC / 8, (const char*)(wt + ws_row(t0, hv, h)), w_row, n);
+    gather(pv, S::DV / 8, (const char*)(v + ((size_t)t0 * hv + h) * DV + cg * kGroupCols), v_row, n);
   };
   auto store_chain = [&](int parity) __attribute__((always_inline)) {
     char VFA_LDS* skw = lds + S::K_OFF + parity * S::KBUF;
@@ -513,18 +522,8 @@ __global__ __launch_bounds__(kChunkWaves * 64) __attribute__((amdgpu_waves_per_e
   auto load_out = [&](int c0) __attribute__((always_inline)) {
     const int n = min(kC, len - c0);
     const int t0 = ts + c0;
-#pragma unroll
-    for (int i = 0; i < S::PK; ++i) {
-      const int e = stid + i * S::STAGERS;
-      const int r = min(e / (DK / 8), n - 1), c8 = e % (DK / 8);
-      pq[i] = *(const u32x4*)(q + ((size_t)(t0 + r) * hqk + hk) * DK + 8 * c8);
-    }
-#pragma unroll
-    for (int i = 0; i < S::PT; ++i) {
-      const int e = stid + i * S::STAGERS;
-      const int r = min(e / (2 * kC / 8), n - 1), c8 = e % (2 * kC / 8);
-      pm[i] = *(const u32x4*)(wm + ws_row(t0 + r, hv, h) + 8 * c8);
-    }
+    gather(pq, DK / 8, (const char*)(q + ((size_t)t0 * hqk + hk) * DK), k_row, n);
+    gather(pm, 2 * kC / 8, (const char*)(wm + ws_row(t0, hv, h)), w_row, n);
     if (stid < kC) {
       const bool ok = stid < n;
       const size_t o = (size_t)(t0 + (ok ? stid : 0)) * hv + h;
