@@ -681,7 +681,6 @@ __global__ __launch_bounds__(kChunkWaves * 64) __attribute__((amdgpu_waves_per_e
       const int n = min(kC, len - c0);
       const int t0 = ts + c0;
       __syncthreads();                  // A: chunk staged, S of this chunk start in sbuf
-      if (c0 + kC < len) load_out(c0 + kC);     // next chunk, in flight during this one
 
       // Q S from the chain wave's published S (hi and lo), scaled by e^gamma.
       f32x4 qs[4] = {};
@@ -704,6 +703,10 @@ __global__ __launch_bounds__(kChunkWaves * 64) __attribute__((amdgpu_waves_per_e
 #pragma unroll
         for (int z = 0; z < 4; ++z) qs[mt][z] *= e1[z];
       }
+      // The next chunk's Q, M and factors go in flight only now: right after
+      // barrier A the address unit is left to the chain waves' loads, which
+      // the chain waits behind.
+      if (c0 + kC < len) load_out(c0 + kC);
       // M operands into registers now: the staging after barrier B overwrites M.
       bf16x8 mh[4][2], ml[4][2];
 #pragma unroll
