@@ -254,9 +254,13 @@ def gated_delta_decode_case(vfa, torch, reps=50, warmup=5):
     ms = time_calls(call, reps, warmup, torch)
     t = median(ms)
     nbytes = 2 * b * hv * d * d * 4
+    # Floor: a device-to-device copy of one state array moves the same bytes (read once, written once).
+    dst = torch.empty_like(s0)
+    tc = median(time_calls(lambda: dst.copy_(s0), reps, warmup, torch))
     res = {"ms_median": round(t, 4), "state_gb": round(nbytes / 1e9, 3), "tb_per_s": round(nbytes / t / 1e9, 3),
-           "frac_hbm": round(nbytes / t / 1e6 / PEAK_HBM_GBPS, 4)}
-    del q, k, v, g, beta, cu, s0, out
+           "frac_hbm": round(nbytes / t / 1e6 / PEAK_HBM_GBPS, 4), "copy_floor_ms": round(tc, 4),
+           "frac_of_copy_rate": round(tc / t, 4)}
+    del q, k, v, g, beta, cu, s0, out, dst
     torch.cuda.empty_cache()
     return res
 
