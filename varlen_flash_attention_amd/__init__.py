@@ -180,6 +180,16 @@ def _check_gpu(name, t, ndim=None):
         raise ValueError(f"{name} must have {ndim} dimensions, got {t.dim()}")
 
 
+def _check_out(name, t, shape, dtype=None):
+    """A caller-supplied output: on the GPU, contiguous, of exactly the shape (and dtype) the kernel
+    writes, so that no launch writes past its end."""
+    _check_gpu(name, t, len(shape))
+    if tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
 def _stream_ptr(device) -> int:
     torch = _torch()
     return int(torch.cuda.current_stream(device).cuda_stream)
@@ -226,11 +236,11 @@ def varlen_attn_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_
     odt = q.dtype if out_dtype is None else out_dtype
     if out is None:
         out = torch.empty((tq, hq, d), dtype=odt, device=q.device)
-    _check_gpu("out", out, 3)
+    _check_out("out", out, (tq, hq, d), None if out_dtype is None else odt)
     out_code = _dtype_code(out)
     if lse is None:
         lse = torch.empty((tq, hq), dtype=torch.float32, device=q.device)
-    _check_gpu("lse", lse, 2)
+    _check_out("lse", lse, (tq, hq), torch.float32)
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     ws_bytes = varlen_attn_fwd_workspace_size(batch, tq, max_seqlen_q, max_seqlen_k, hq, hkv, d)
     if ws_bytes and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
@@ -273,9 +283,11 @@ def attn_update(lse, go, update_type: int = 1, out=None, lse_out=None):
     code = _dtype_code(go)
     if out is None:
         out = torch.empty((bsh, hd), dtype=go.dtype, device=go.device)
-    _check_gpu("out", out, 2)
+    _check_out("out", out, (bsh, hd), go.dtype)
     if update_type == 1 and lse_out is None:
         lse_out = torch.empty((bsh,), dtype=torch.float32, device=go.device)
+    if update_type == 1:
+        _check_out("lse_out", lse_out, (bsh,), torch.float32)
     st = lib.attn_update(lse.data_ptr(), go.data_ptr(), code, sp, bsh, hd, int(update_type), out.data_ptr(),
                          lse_out.data_ptr() if (update_type == 1 and lse_out is not None) else None,
                          _stream_ptr(go.device))
@@ -298,7 +310,7 @@ def varlen_last_token_gather(x, cu_seqlens, out=None):
         row *= int(s)
     if out is None:
         out = torch.empty((batch, *x.shape[1:]), dtype=x.dtype, device=x.device)
-    _check_gpu("out", out)
+    _check_out("out", out, (batch, *x.shape[1:]), x.dtype)
     st = lib.varlen_last_token_gather(x.data_ptr(), _dtype_code(x), cu_seqlens.data_ptr(), batch, row,
                                       out.data_ptr(), _stream_ptr(x.device))
     if st != 0:
@@ -350,10 +362,10 @@ def paged_attn_decode(q, k_cache, v_cache, block_table, cu_seqlens_q, seqused_k,
     odt = q.dtype if out_dtype is None else out_dtype
     if out is None:
         out = torch.empty((tq, hq, d), dtype=odt, device=q.device)
-    _check_gpu("out", out, 3)
+    _check_out("out", out, (tq, hq, d), None if out_dtype is None else odt)
     if lse is None:
         lse = torch.empty((tq, hq), dtype=torch.float32, device=q.device)
-    _check_gpu("lse", lse, 2)
+    _check_out("lse", lse, (tq, hq), torch.float32)
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     ws_bytes = paged_attn_decode_workspace_size(batch, tq, max_seqlen_q, max_seqlen_k, hq, hkv, d)
     if ws_bytes and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
@@ -396,8 +408,8 @@ def qk_norm_rope(q, k, q_weight, k_weight, cos, sin, eps: float = 1e-6, q_out=No
         q_out = torch.empty_like(q)
     if k_out is None:
         k_out = torch.empty_like(k)
-    _check_gpu("q_out", q_out, 3)
-    _check_gpu("k_out", k_out, 3)
+    _check_out("q_out", q_out, tuple(q.shape), q.dtype)
+    _check_out("k_out", k_out, tuple(k.shape), k.dtype)
     st = lib.qk_norm_rope(q.data_ptr(), k.data_ptr(), VFA_BF16, q_weight.data_ptr(), k_weight.data_ptr(),
                           cos.data_ptr(), sin.data_ptr(), t, hq, int(k.shape[1]), d, float(eps), q_out.data_ptr(),
                           k_out.data_ptr(), _stream_ptr(q.device))
@@ -443,7 +455,7 @@ def gated_delta_rule_fwd(q, k, v, g, beta, cu_seqlens, max_seqlen: int, scale: f
             raise ValueError(f"initial_state must be float32 [{batch}, {hv}, {dk}, {dv}]")
     if out is None:
         out = torch.empty((tt, hv, dv), dtype=torch.bfloat16, device=q.device)
-    _check_gpu("out", out, 3)
+    _check_out("out", out, (tt, hv, dv), torch.bfloat16)
     final = torch.empty((batch, hv, dk, dv), dtype=torch.float32, device=q.device) if output_final_state else None
     sc = 1.0 / math.sqrt(dk) if scale is None else float(scale)
     ws_bytes = gated_delta_rule_fwd_workspace_size(tt, hv, max_seqlen)
