@@ -1,5 +1,5 @@
-"""The Python binding rejects caller-supplied outputs of the wrong shape or dtype before any launch
-(the kernels write exactly the shape they are given pointers for)."""
+"""The Python binding rejects caller-supplied outputs of the wrong shape or dtype, and weights of the
+wrong length, before any launch (the kernels touch exactly the shapes they are given pointers for)."""
 import numpy as np
 import pytest
 
@@ -36,6 +36,8 @@ def test_outputs_of_wrong_shape_or_dtype_are_rejected():
     cs = torch.zeros((8, 128), dtype=f32, device=dev)
     with pytest.raises(ValueError):
         vfa.qk_norm_rope(q, kv, w, w, cs, cs, q_out=torch.empty((8, 2, 128), dtype=bf, device=dev))
+    with pytest.raises(ValueError):
+        vfa.qk_norm_rope(q, kv, w[:64], w, cs, cs)
     g = torch.zeros((8, 4), dtype=f32, device=dev)
     gk = torch.zeros((8, 2, 128), dtype=bf, device=dev)
     with pytest.raises(ValueError):

@@ -404,6 +404,8 @@ def qk_norm_rope(q, k, q_weight, k_weight, cos, sin, eps: float = 1e-6, q_out=No
         raise ValueError("q and k must share the token count and head_dim")
     if tuple(cos.shape) != (t, d) or tuple(sin.shape) != (t, d):
         raise ValueError(f"cos and sin must be [{t}, {d}]")
+    if int(q_weight.shape[0]) != d or int(k_weight.shape[0]) != d:
+        raise ValueError(f"q_weight and k_weight must have {d} entries")
     if q_out is None:
         q_out = torch.empty_like(q)
     if k_out is None:
