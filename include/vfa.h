@@ -27,8 +27,11 @@
  *         [0, num_pages).
  *     A violation returns VFA_ERR_SHAPE and launches nothing. The check
  *     synchronises the stream, copies one word to the host and clears a
- *     library word in device memory with hipMemsetAsync. Debug calls must not
- *     be captured into a graph or run concurrently on one device.
+ *     library word in device memory with hipMemsetAsync. Checked calls are
+ *     serialised process-wide by a host lock (calls on several streams or
+ *     threads each see only their own violations). A checked call on a
+ *     stream that is capturing a graph returns VFA_ERR_UNSUPPORTED and
+ *     launches nothing, leaving the capture intact.
  *
  * The argument conventions follow the problem as the source pages state it:
  *   [P1] "From GPU to NPU: Qwen3-Embedding model adaptation and performance

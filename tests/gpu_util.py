@@ -93,3 +93,20 @@ def sample_tokens(w, per_seq=4, seed=0, limit=None):
     if limit is not None and len(toks) > limit:
         toks = np.sort(rng.choice(toks, limit, replace=False))
     return toks
+
+
+def tile_tokens(w, tile, seed=0):
+    """One seeded token from every `tile`-token query tile of every sequence, plus each sequence's first
+    and last token (sorted, unique): with `tile` the kernel's tokens per workgroup, every workgroup of
+    the call has a row in the sample."""
+    rng = np.random.default_rng(seed)
+    cu = w.cu_seqlens_q.astype(np.int64)
+    toks = []
+    for b in range(w.batch):
+        lo, hi = int(cu[b]), int(cu[b + 1])
+        if hi <= lo:
+            continue
+        toks += [lo, hi - 1]
+        for t0 in range(lo, hi, tile):
+            toks.append(int(rng.integers(t0, min(hi, t0 + tile))))
+    return np.unique(np.array(toks, dtype=np.int64))

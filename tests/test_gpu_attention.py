@@ -10,7 +10,7 @@ import pytest
 import oracle
 import varlen_flash_attention_amd as vfa
 from varlen_flash_attention_amd.workloads import make_custom, make_workload
-from tests.gpu_util import check, host64, need_gpu, sample_tokens, to_device
+from tests.gpu_util import check, host64, need_gpu, tile_tokens, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -75,21 +75,43 @@ def test_embed_prefill_full_with_gather():
     assert tuple(last.shape) == (64, 16, 128)
 
 
+# The launcher takes 256-column workgroups (eight waves) once sequences average
+# at least eight of their query tiles, i.e. mean Lq >= 8 * 256 / G tokens, and
+# 128-column workgroups (four waves) below that.
+def wide_shape(w):
+    return w.total_q // w.batch >= 8 * (256 // (w.num_heads_q // w.num_heads_kv))
+
+
 @pytest.mark.parametrize("causal", [True, False])
-def test_long_prefill_small(causal):
+def test_long_prefill_small_four_wave(causal):
     w = make_custom([300, 513, 1029, 77], num_heads_q=32, num_heads_kv=8, head_dim=128, dtype="bf16",
                     causal=causal, seed=31, name="long_small")
-    full_check(f"long_prefill_small causal={causal}", w)
+    assert not wide_shape(w)
+    full_check(f"long_prefill_small (4-wave shape) causal={causal}", w)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_long_prefill_small_eight_wave(causal):
+    # The headline shape (Hq 32, Hkv 8, D 128, bf16) with ragged tails, on the eight-wave kernel.
+    w = make_custom([1300, 513, 1029, 77, 700, 1500], num_heads_q=32, num_heads_kv=8, head_dim=128, dtype="bf16",
+                    causal=causal, seed=32, name="long_small_wide")
+    assert wide_shape(w)
+    full_check(f"long_prefill_small (8-wave shape) causal={causal}", w)
 
 
 @pytest.mark.parametrize("name", ["long_prefill", "long_prefill_full"])
-def test_long_prefill_full_size_sampled(name):
+def test_long_prefill_full_size_every_tile(name):
+    # Full size, in the launch configuration the benchmark times: one token from every 64-token query
+    # tile (256 columns / G = 4 heads, one workgroup per tile and kv head) plus each sequence's first
+    # and last token, all 32 heads, element by element against the oracle.
     w = make_workload(name)
+    assert wide_shape(w)
     print(f"[case] {name} full size: lengths={w.lengths_q.tolist()} Tq={w.total_q}", flush=True)
     out, lse = run_gpu(w)
-    toks = sample_tokens(w, per_seq=6, seed=3, limit=160)
+    toks = tile_tokens(w, 64, seed=3)
     o_ref, l_ref = run_oracle(w, tokens=toks)
-    check(f"{name} (sampled {len(toks)} tokens)", host64(out)[toks], host64(lse)[toks], o_ref, l_ref, "bf16")
+    check(f"{name} ({len(toks)} tokens, every query tile)", host64(out)[toks], host64(lse)[toks], o_ref, l_ref,
+          "bf16")
 
 
 @pytest.mark.parametrize("causal", [True, False])

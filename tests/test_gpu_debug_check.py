@@ -65,3 +65,31 @@ def test_debug_check_gather(monkeypatch):
     with pytest.raises(vfa.VfaError) as e:
         vfa.varlen_last_token_gather(x, _cu(torch, [0, 9, 5]))
     assert e.value.status == 2
+
+
+def test_debug_check_refused_under_graph_capture(monkeypatch):
+    # The check synchronises its stream, which graph capture forbids: a checked call on a capturing
+    # stream returns VFA_ERR_UNSUPPORTED before touching the stream, and the capture stays usable.
+    torch = need_gpu()
+    q, k, v = _inputs(torch, 20)
+    cu = _cu(torch, [0, 12, 20])
+    out = torch.empty((20, 4, 64), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((20, 4), dtype=torch.float32, device="cuda")
+    ref_o, ref_l = vfa.varlen_attn_fwd(q, k, v, cu, cu, 12, 12)
+    torch.cuda.synchronize()
+    print("[case] VFA_DEBUG under graph capture", flush=True)
+    monkeypatch.setenv("VFA_DEBUG", "1")
+    g = torch.cuda.CUDAGraph()
+    status = None
+    with torch.cuda.graph(g):
+        try:
+            vfa.varlen_attn_fwd(q, k, v, cu, cu, 12, 12, out=out, lse=lse)
+        except vfa.VfaError as e:
+            status = e.status
+        monkeypatch.setenv("VFA_DEBUG", "0")
+        vfa.varlen_attn_fwd(q, k, v, cu, cu, 12, 12, out=out, lse=lse)   # unchecked: captured as usual
+    assert status == 3
+    out.zero_()
+    g.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref_o) and torch.equal(lse, ref_l)

@@ -171,23 +171,44 @@ def _dtype_code(t) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}; expected float32 or bfloat16")
 
 
-def _check_gpu(name, t, ndim=None):
+def _check_gpu(name, t, ndim=None, device=None):
+    """A tensor the kernels read or write: on the GPU (on `device` when given: one call runs on one
+    device), contiguous, and of `ndim` dimensions when given."""
     if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor (libvfa has no CPU path)")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the call runs on {device}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if ndim is not None and t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dimensions, got {t.dim()}")
 
 
-def _check_out(name, t, shape, dtype=None):
-    """A caller-supplied output: on the GPU, contiguous, of exactly the shape (and dtype) the kernel
-    writes, so that no launch writes past its end."""
-    _check_gpu(name, t, len(shape))
+def _check_out(name, t, shape, dtype=None, device=None):
+    """A caller-supplied output: on the call's GPU, contiguous, of exactly the shape (and dtype) the
+    kernel writes, so that no launch writes past its end."""
+    _check_gpu(name, t, len(shape), device)
     if tuple(t.shape) != tuple(int(x) for x in shape):
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
     if dtype is not None and t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _workspace(workspace, need: int, device):
+    """The split kernels' partials buffer: None when the call needs none; a fresh uint8 buffer when the
+    caller gives none; else the caller's, which must be a contiguous 1-D uint8 tensor on the call's
+    device holding at least `need` bytes (the kernels write up to `need` bytes through its pointer)."""
+    torch = _torch()
+    if need <= 0:
+        return None
+    if workspace is None:
+        return torch.empty(need, dtype=torch.uint8, device=device)
+    _check_gpu("workspace", workspace, 1, device)
+    if workspace.dtype != torch.uint8:
+        raise TypeError(f"workspace must be uint8, got {workspace.dtype}")
+    if workspace.numel() < need:
+        raise ValueError(f"workspace holds {workspace.numel()} bytes, the call needs {need}")
+    return workspace
 
 
 def _stream_ptr(device) -> int:
@@ -215,10 +236,11 @@ def varlen_attn_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_
     """
     torch = _torch()
     lib = load_library()
+    dev = q.device
     for name, t in (("q", q), ("k", k), ("v", v)):
-        _check_gpu(name, t, 3)
+        _check_gpu(name, t, 3, dev)
     for name, t in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
-        _check_gpu(name, t, 1)
+        _check_gpu(name, t, 1, dev)
         if t.dtype != torch.int32:
             raise TypeError(f"{name} must be int32")
     if k.dtype != q.dtype or v.dtype != q.dtype:
@@ -236,16 +258,15 @@ def varlen_attn_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_
     odt = q.dtype if out_dtype is None else out_dtype
     if out is None:
         out = torch.empty((tq, hq, d), dtype=odt, device=q.device)
-    _check_out("out", out, (tq, hq, d), None if out_dtype is None else odt)
+    _check_out("out", out, (tq, hq, d), None if out_dtype is None else odt, dev)
     out_code = _dtype_code(out)
     if lse is None:
         lse = torch.empty((tq, hq), dtype=torch.float32, device=q.device)
-    _check_out("lse", lse, (tq, hq), torch.float32)
+    _check_out("lse", lse, (tq, hq), torch.float32, dev)
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     ws_bytes = varlen_attn_fwd_workspace_size(batch, tq, max_seqlen_q, max_seqlen_k, hq, hkv, d)
-    if ws_bytes and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
-    ws_ptr = workspace.data_ptr() if (ws_bytes and workspace is not None) else None
+    workspace = _workspace(workspace, ws_bytes, dev)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
     if causal_offset is None:
         st = lib.varlen_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), in_code,
                                  cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(),
@@ -255,7 +276,7 @@ def varlen_attn_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_
         if st != 0:
             raise VfaError(st, "varlen_attn_fwd")
         return out, lse
-    _check_gpu("causal_offset", causal_offset, 1)
+    _check_gpu("causal_offset", causal_offset, 1, dev)
     if causal_offset.dtype != torch.int32 or int(causal_offset.shape[0]) != batch:
         raise ValueError("causal_offset must be int32 with one entry per sequence")
     st = lib.varlen_attn_fwd_offset(q.data_ptr(), k.data_ptr(), v.data_ptr(), in_code,
@@ -272,8 +293,8 @@ def attn_update(lse, go, update_type: int = 1, out=None, lse_out=None):
     """Merge sp partials: lse [sp, bsh] fp32, go [sp, bsh, hd] -> (out [bsh, hd], lse_out [bsh] | None)."""
     torch = _torch()
     lib = load_library()
-    _check_gpu("lse", lse, 2)
     _check_gpu("go", go, 3)
+    _check_gpu("lse", lse, 2, go.device)
     if lse.dtype != torch.float32:
         raise TypeError("lse must be float32")
     sp, bsh = int(lse.shape[0]), int(lse.shape[1])
@@ -283,11 +304,11 @@ def attn_update(lse, go, update_type: int = 1, out=None, lse_out=None):
     code = _dtype_code(go)
     if out is None:
         out = torch.empty((bsh, hd), dtype=go.dtype, device=go.device)
-    _check_out("out", out, (bsh, hd), go.dtype)
+    _check_out("out", out, (bsh, hd), go.dtype, go.device)
     if update_type == 1 and lse_out is None:
         lse_out = torch.empty((bsh,), dtype=torch.float32, device=go.device)
     if update_type == 1:
-        _check_out("lse_out", lse_out, (bsh,), torch.float32)
+        _check_out("lse_out", lse_out, (bsh,), torch.float32, go.device)
     st = lib.attn_update(lse.data_ptr(), go.data_ptr(), code, sp, bsh, hd, int(update_type), out.data_ptr(),
                          lse_out.data_ptr() if (update_type == 1 and lse_out is not None) else None,
                          _stream_ptr(go.device))
@@ -301,7 +322,7 @@ def varlen_last_token_gather(x, cu_seqlens, out=None):
     torch = _torch()
     lib = load_library()
     _check_gpu("x", x)
-    _check_gpu("cu_seqlens", cu_seqlens, 1)
+    _check_gpu("cu_seqlens", cu_seqlens, 1, x.device)
     if cu_seqlens.dtype != torch.int32:
         raise TypeError("cu_seqlens must be int32")
     batch = int(cu_seqlens.shape[0]) - 1
@@ -310,7 +331,7 @@ def varlen_last_token_gather(x, cu_seqlens, out=None):
         row *= int(s)
     if out is None:
         out = torch.empty((batch, *x.shape[1:]), dtype=x.dtype, device=x.device)
-    _check_out("out", out, (batch, *x.shape[1:]), x.dtype)
+    _check_out("out", out, (batch, *x.shape[1:]), x.dtype, x.device)
     st = lib.varlen_last_token_gather(x.data_ptr(), _dtype_code(x), cu_seqlens.data_ptr(), batch, row,
                                       out.data_ptr(), _stream_ptr(x.device))
     if st != 0:
@@ -337,12 +358,13 @@ def paged_attn_decode(q, k_cache, v_cache, block_table, cu_seqlens_q, seqused_k,
     """
     torch = _torch()
     lib = load_library()
+    dev = q.device
     _check_gpu("q", q, 3)
     for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
-        _check_gpu(name, t, 4)
-    _check_gpu("block_table", block_table, 2)
+        _check_gpu(name, t, 4, dev)
+    _check_gpu("block_table", block_table, 2, dev)
     for name, t in (("cu_seqlens_q", cu_seqlens_q), ("seqused_k", seqused_k)):
-        _check_gpu(name, t, 1)
+        _check_gpu(name, t, 1, dev)
     for name, t in (("block_table", block_table), ("cu_seqlens_q", cu_seqlens_q), ("seqused_k", seqused_k)):
         if t.dtype != torch.int32:
             raise TypeError(f"{name} must be int32")
@@ -362,15 +384,14 @@ def paged_attn_decode(q, k_cache, v_cache, block_table, cu_seqlens_q, seqused_k,
     odt = q.dtype if out_dtype is None else out_dtype
     if out is None:
         out = torch.empty((tq, hq, d), dtype=odt, device=q.device)
-    _check_out("out", out, (tq, hq, d), None if out_dtype is None else odt)
+    _check_out("out", out, (tq, hq, d), None if out_dtype is None else odt, dev)
     if lse is None:
         lse = torch.empty((tq, hq), dtype=torch.float32, device=q.device)
-    _check_out("lse", lse, (tq, hq), torch.float32)
+    _check_out("lse", lse, (tq, hq), torch.float32, dev)
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     ws_bytes = paged_attn_decode_workspace_size(batch, tq, max_seqlen_q, max_seqlen_k, hq, hkv, d)
-    if ws_bytes and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
-    ws_ptr = workspace.data_ptr() if (ws_bytes and workspace is not None) else None
+    workspace = _workspace(workspace, ws_bytes, dev)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
     st = lib.paged_attn_decode(q.data_ptr(), in_code, k_cache.data_ptr(), v_cache.data_ptr(),
                                block_table.data_ptr(), max_pages, num_pages, page_size,
                                cu_seqlens_q.data_ptr(), seqused_k.data_ptr(),
@@ -387,12 +408,13 @@ def qk_norm_rope(q, k, q_weight, k_weight, cos, sin, eps: float = 1e-6, q_out=No
     embedding with fp32 cos / sin [T, D]. Returns (q_out, k_out); pass q_out=q, k_out=k to work in place."""
     torch = _torch()
     lib = load_library()
+    dev = q.device
     _check_gpu("q", q, 3)
-    _check_gpu("k", k, 3)
+    _check_gpu("k", k, 3, dev)
     for name, t in (("q_weight", q_weight), ("k_weight", k_weight)):
-        _check_gpu(name, t, 1)
+        _check_gpu(name, t, 1, dev)
     for name, t in (("cos", cos), ("sin", sin)):
-        _check_gpu(name, t, 2)
+        _check_gpu(name, t, 2, dev)
         if t.dtype != torch.float32:
             raise TypeError(f"{name} must be float32")
     if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16:
@@ -410,8 +432,8 @@ def qk_norm_rope(q, k, q_weight, k_weight, cos, sin, eps: float = 1e-6, q_out=No
         q_out = torch.empty_like(q)
     if k_out is None:
         k_out = torch.empty_like(k)
-    _check_out("q_out", q_out, tuple(q.shape), q.dtype)
-    _check_out("k_out", k_out, tuple(k.shape), k.dtype)
+    _check_out("q_out", q_out, tuple(q.shape), q.dtype, dev)
+    _check_out("k_out", k_out, tuple(k.shape), k.dtype, dev)
     st = lib.qk_norm_rope(q.data_ptr(), k.data_ptr(), VFA_BF16, q_weight.data_ptr(), k_weight.data_ptr(),
                           cos.data_ptr(), sin.data_ptr(), t, hq, int(k.shape[1]), d, float(eps), q_out.data_ptr(),
                           k_out.data_ptr(), _stream_ptr(q.device))
@@ -433,15 +455,16 @@ def gated_delta_rule_fwd(q, k, v, g, beta, cu_seqlens, max_seqlen: int, scale: f
     Default scale 1/sqrt(Dk). Returns (out [T, Hv, Dv] bf16, final_state [B, Hv, Dk, Dv] fp32 or None)."""
     torch = _torch()
     lib = load_library()
+    dev = q.device
     for name, t in (("q", q), ("k", k), ("v", v)):
-        _check_gpu(name, t, 3)
+        _check_gpu(name, t, 3, dev)
         if t.dtype != torch.bfloat16:
             raise TypeError(f"{name} must be bfloat16")
     for name, t in (("g", g), ("beta", beta)):
-        _check_gpu(name, t, 2)
+        _check_gpu(name, t, 2, dev)
         if t.dtype != torch.float32:
             raise TypeError(f"{name} must be float32")
-    _check_gpu("cu_seqlens", cu_seqlens, 1)
+    _check_gpu("cu_seqlens", cu_seqlens, 1, dev)
     if cu_seqlens.dtype != torch.int32:
         raise TypeError("cu_seqlens must be int32")
     tt, hqk, dk = (int(x) for x in q.shape)
@@ -452,12 +475,12 @@ def gated_delta_rule_fwd(q, k, v, g, beta, cu_seqlens, max_seqlen: int, scale: f
         raise ValueError(f"g and beta must be [{tt}, {hv}]")
     batch = int(cu_seqlens.shape[0]) - 1
     if initial_state is not None:
-        _check_gpu("initial_state", initial_state, 4)
+        _check_gpu("initial_state", initial_state, 4, dev)
         if initial_state.dtype != torch.float32 or tuple(initial_state.shape) != (batch, hv, dk, dv):
             raise ValueError(f"initial_state must be float32 [{batch}, {hv}, {dk}, {dv}]")
     if out is None:
         out = torch.empty((tt, hv, dv), dtype=torch.bfloat16, device=q.device)
-    _check_out("out", out, (tt, hv, dv), torch.bfloat16)
+    _check_out("out", out, (tt, hv, dv), torch.bfloat16, dev)
     final = torch.empty((batch, hv, dk, dv), dtype=torch.float32, device=q.device) if output_final_state else None
     sc = 1.0 / math.sqrt(dk) if scale is None else float(scale)
     ws_bytes = gated_delta_rule_fwd_workspace_size(tt, hv, max_seqlen)

@@ -79,6 +79,16 @@ bool debug_checks() {
   return e && *e && std::strcmp(e, "0") != 0;
 }
 
+// Status of a VFA_DEBUG contract check: violated -> VFA_ERR_SHAPE; asked for
+// on a stream that is capturing a graph (the check must synchronise) ->
+// VFA_ERR_UNSUPPORTED; a HIP error -> VFA_ERR_LAUNCH.
+int32_t debug_status(int r) {
+  if (r == 0) return VFA_OK;
+  if (r == 1) return VFA_ERR_SHAPE;
+  if (r == -2) return VFA_ERR_UNSUPPORTED;
+  return VFA_ERR_LAUNCH;
+}
+
 }  // namespace
 
 VFA_API int32_t vfa_abi_version(void) { return VFA_ABI_VERSION; }
@@ -133,8 +143,7 @@ int32_t attn_fwd_impl(const void* q, const void* k, const void* v, int32_t in_dt
   if (debug_checks()) {
     const int r = vfa::check_cu_seqlens(cu_seqlens_q, total_q, max_seqlen_q, cu_seqlens_k, total_k, max_seqlen_k,
                                         batch, stream);
-    if (r < 0) return VFA_ERR_LAUNCH;
-    if (r > 0) return VFA_ERR_SHAPE;
+    if (r != 0) return debug_status(r);
   }
 
   vfa::AttnArgs a{};
@@ -208,8 +217,7 @@ VFA_API int32_t varlen_last_token_gather(const void* x, int32_t dtype, const int
   if (dtype != VFA_F32 && dtype != VFA_BF16) return VFA_ERR_UNSUPPORTED;
   if (debug_checks()) {
     const int r = vfa::check_cu_seqlens(cu_seqlens, -1, 0x7fffffff, nullptr, 0, 0, batch, stream);
-    if (r < 0) return VFA_ERR_LAUNCH;
-    if (r > 0) return VFA_ERR_SHAPE;
+    if (r != 0) return debug_status(r);
   }
   return vfa::launch_last_token_gather(x, dtype == VFA_F32 ? 4 : 2, cu_seqlens, batch, row_elems, out, stream) == 0
              ? VFA_OK
@@ -258,8 +266,7 @@ VFA_API int32_t paged_attn_decode(const void* q, int32_t in_dtype, const void* k
     if (r == 0)
       r = vfa::check_paged(seqused_k, block_table, batch, max_pages_per_seq, page_size, num_pages, max_seqlen_k,
                            stream);
-    if (r < 0) return VFA_ERR_LAUNCH;
-    if (r > 0) return VFA_ERR_SHAPE;
+    if (r != 0) return debug_status(r);
   }
 
   vfa::PagedArgs a{};
@@ -334,8 +341,7 @@ VFA_API int32_t gated_delta_rule_fwd(const void* q, const void* k, const void* v
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace))) return VFA_ERR_WORKSPACE;
   if (debug_checks()) {
     const int r = vfa::check_cu_seqlens(cu_seqlens, total_tokens, max_seqlen, nullptr, 0, 0, batch, stream);
-    if (r < 0) return VFA_ERR_LAUNCH;
-    if (r > 0) return VFA_ERR_SHAPE;
+    if (r != 0) return debug_status(r);
   }
   vfa::GatedDeltaArgs a{};
   a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.cu = cu_seqlens;

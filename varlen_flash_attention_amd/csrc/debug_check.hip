@@ -6,14 +6,28 @@
 // Ascend", core optimisation 1: cu_seqlens holds the running token count,
 // starting at 0, non-decreasing, ending at the total; every sequence fits the
 // host's max_seqlen bound.
+#include <mutex>
+
 #include "common.h"
 #include "launch.h"
 
 namespace vfa {
 namespace {
 
-// Violation bits of the last checked call on this device (one word per device).
+// Violation bits of the checked call in progress on this device (one word per
+// device). Checked calls are serialised by g_check_mutex, so two of them on
+// different streams never share the word at the same time.
 __device__ int g_contract_bits;
+std::mutex g_check_mutex;
+
+// The check synchronises its stream, which a stream under graph capture does
+// not allow: report that instead of breaking the capture. Returns 0 when the
+// stream is not capturing, -2 when it is, -1 on a HIP error.
+int capture_state(hipStream_t st) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(st, &cs) != hipSuccess) return -1;
+  return cs == hipStreamCaptureStatusNone ? 0 : -2;
+}
 
 // One workgroup: thread t checks entries t, t + 256, ... of cu[0 .. batch].
 // total < 0 skips the end check; every index stays within cu[0 .. batch].
@@ -72,6 +86,8 @@ int read_contract_word(const int* bits, hipStream_t st) {
 int check_cu_seqlens(const int32_t* cu_a, int total_a, int max_a, const int32_t* cu_b, int total_b, int max_b,
                      int batch, void* stream) {
   hipStream_t st = (hipStream_t)stream;
+  if (const int c = capture_state(st)) return c;
+  std::lock_guard<std::mutex> hold(g_check_mutex);
   int* bits = contract_word(st);
   if (!bits) return -1;
   hipLaunchKernelGGL(check_cu_kernel, dim3(1), dim3(256), 0, st, cu_a, batch, total_a, max_a, bits);
@@ -82,6 +98,8 @@ int check_cu_seqlens(const int32_t* cu_a, int total_a, int max_a, const int32_t*
 int check_paged(const int32_t* seqused_k, const int32_t* block_table, int batch, int max_pages, int page_size,
                 int num_pages, int max_seqlen_k, void* stream) {
   hipStream_t st = (hipStream_t)stream;
+  if (const int c = capture_state(st)) return c;
+  std::lock_guard<std::mutex> hold(g_check_mutex);
   int* bits = contract_word(st);
   if (!bits) return -1;
   hipLaunchKernelGGL(check_paged_kernel, dim3((unsigned)batch), dim3(256), 0, st, seqused_k, block_table, max_pages,

@@ -120,14 +120,15 @@ int launch_last_token_gather(const void* x, int esize, const int32_t* cu, int ba
 
 // Caller-contract check of one or two cu_seqlens arrays of batch + 1 entries
 // (cu_b may be NULL; a negative total skips the end check). Synchronises the
-// stream. Returns 0 if the contract holds, 1 if it is violated, -1 on a HIP
-// error.
+// stream; checked calls are serialised process-wide. Returns 0 if the
+// contract holds, 1 if it is violated, -1 on a HIP error, -2 (nothing
+// launched) if the stream is capturing a graph.
 int check_cu_seqlens(const int32_t* cu_a, int total_a, int max_a, const int32_t* cu_b, int total_b, int max_b,
                      int batch, void* stream);
 
 // Caller-contract check of the paged inputs: 0 <= seqused_k[b] <= max_seqlen_k
 // and every block-table entry that names one of those keys' pages lies in
-// [0, num_pages). Synchronises the stream; same return values.
+// [0, num_pages). Synchronises the stream; same serialisation and return values.
 int check_paged(const int32_t* seqused_k, const int32_t* block_table, int batch, int max_pages, int page_size,
                 int num_pages, int max_seqlen_k, void* stream);
 
