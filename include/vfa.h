@@ -6,7 +6,9 @@
  *   - Tensor arguments are DEVICE pointers to contiguous row-major buffers
  *     that the caller allocates, owns and frees. The library never allocates,
  *     frees, synchronises or copies device memory to the host, and keeps no
- *     state between calls (it is reentrant).
+ *     state between calls (it is reentrant). The one exception is
+ *     varlen_attn_fwd_noalloc, whose split-KV partials live in a static
+ *     per-device array (see there).
  *   - `stream` is a hipStream_t (NULL = the null stream). Work is enqueued
  *     on it asynchronously; results are ready when the stream reaches them.
  *   - Sizes and flags are HOST values. Every condition that can be checked
@@ -57,7 +59,7 @@
 extern "C" {
 #endif
 
-#define VFA_ABI_VERSION 6
+#define VFA_ABI_VERSION 7
 
 typedef enum vfa_status {
   VFA_OK = 0,
@@ -165,6 +167,40 @@ int32_t varlen_attn_fwd_offset(const void* q, const void* k, const void* v, int3
                                float softmax_scale, int32_t causal,
                                void* out, int32_t out_dtype, float* lse,
                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of the library's static scratch array on each device: the most
+ * split-KV partial storage varlen_attn_fwd_noalloc can use. */
+#define VFA_STATIC_SCRATCH_BYTES (16u << 20)
+
+/* varlen_attn_fwd for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. It takes no workspace: the split-KV partials go to a static
+ * device array of VFA_STATIC_SCRATCH_BYTES (16 MiB) that every device the
+ * library runs on holds from the moment the library's code is loaded there
+ * until the process ends. The call itself allocates and frees nothing and
+ * calls no allocating library routine; the first call on a device looks up
+ * that device's copy of the array (hipGetSymbolAddress) and caches it.
+ *
+ * Arguments, results, the supported set and the error codes are those of
+ * varlen_attn_fwd without workspace / workspace_bytes, plus:
+ *   - VFA_ERR_WORKSPACE if the call needs more split-KV storage than the
+ *     static array holds, i.e. varlen_attn_fwd_workspace_size(...) >
+ *     VFA_STATIC_SCRATCH_BYTES (the decode shape of 64 sequences x 32 heads
+ *     with keys up to 32768 needs 8.5 MB). Nothing is launched.
+ *   - VFA_ERR_LAUNCH if the array's address cannot be looked up.
+ * Every call on one device shares that device's array, and each call's
+ * kernels write every byte of it they read, so no state carries over
+ * between calls. Calls that overlap on one device (several streams or
+ * threads at once) race on the array: serialise them, or use
+ * varlen_attn_fwd with a workspace per stream.
+ */
+int32_t varlen_attn_fwd_noalloc(const void* q, const void* k, const void* v, int32_t in_dtype,
+                                const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                int32_t batch, int32_t total_q, int32_t total_k,
+                                int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                                float softmax_scale, int32_t causal,
+                                void* out, int32_t out_dtype, float* lse, void* stream);
 
 /* AttentionUpdate merge ([P4], operator function description):
  *   lse_max = max_i lse[i, r]

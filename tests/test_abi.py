@@ -44,7 +44,7 @@ def test_exports_match_header(lib):
 
 
 def test_abi_version(lib):
-    assert lib.vfa_abi_version() == vfa._header_abi_version() == 6
+    assert lib.vfa_abi_version() == vfa._header_abi_version() == 7
 
 
 def test_status_strings(lib):
@@ -115,6 +115,45 @@ def test_fwd_offset_validation(lib):
     assert off(*a, None, 0, 8, 8, 4, 4, 4, 2, 128, 0.125, 1, *tail) == OK   # empty batch
     assert off(*a, P, 2, 8, 8, 4, 4, 4, 2, 96, 0.125, 1, *tail) == UNSUP     # same checks as varlen_attn_fwd
     assert off(*a, P, -1, 8, 8, 4, 4, 4, 2, 128, 0.125, 1, *tail) == SHAPE
+
+
+def _noalloc(lib, **kw):
+    a = dict(q=P, k=P, v=P, in_dtype=BF16, cu_q=P, cu_k=P, batch=2, total_q=8, total_k=8, max_q=4, max_k=4,
+             hq=4, hkv=2, d=128, scale=0.125, causal=1, out=P, out_dtype=BF16, lse=P, stream=None)
+    a.update(kw)
+    return lib.varlen_attn_fwd_noalloc(a["q"], a["k"], a["v"], a["in_dtype"], a["cu_q"], a["cu_k"], a["batch"],
+                                       a["total_q"], a["total_k"], a["max_q"], a["max_k"], a["hq"], a["hkv"],
+                                       a["d"], a["scale"], a["causal"], a["out"], a["out_dtype"], a["lse"],
+                                       a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=0), OK),
+    (dict(batch=-1), SHAPE),
+    (dict(q=None), NULL),
+    (dict(lse=None), NULL),
+    (dict(hq=6, hkv=4), SHAPE),
+    (dict(d=96), UNSUP),
+    (dict(in_dtype=F32, out_dtype=BF16), UNSUP),
+    (dict(out=P + 8), UNSUP),
+    # 256 decode sequences with keys up to 32768 in 4096-key splits: 8 * 256 * 32 * 129 * 4 B = 33.8 MB of
+    # partials, more than the 16 MiB static array holds
+    (dict(batch=256, total_q=256, total_k=256 * 32768, max_q=1, max_k=32768, hq=32, hkv=4), WS),
+])
+def test_noalloc_validation(lib, kw, code):
+    # The same checks as varlen_attn_fwd, and a call whose split-KV partials exceed the static array is
+    # rejected before anything is launched (or looked up).
+    assert _noalloc(lib, **kw) == code
+
+
+def test_noalloc_limit_matches_the_workspace_plan(lib):
+    limit = vfa.STATIC_SCRATCH_BYTES
+    with open(HEADER) as fh:
+        assert re.search(r"#define\s+VFA_STATIC_SCRATCH_BYTES\s+\(16u << 20\)", fh.read())
+    assert limit == 16 << 20
+    ws = lib.varlen_attn_fwd_workspace_size
+    assert ws(64, 64, 1, 32768, 32, 4, 128) <= limit            # the decode workload fits
+    assert ws(256, 256, 1, 32768, 32, 4, 128) > limit           # the case rejected above does not
 
 
 def _upd(lib, **kw):

@@ -12,6 +12,9 @@ Entry points (same names as the C ABI in include/vfa.h):
   varlen_attn_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
                   softmax_scale=None, causal=True, out_dtype=None, causal_offset=None) -> (out, lse)
       (with causal_offset given: the C entry point varlen_attn_fwd_offset)
+  varlen_attn_fwd_noalloc(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, out, lse,
+                          softmax_scale=None, causal=True) -> (out, lse)
+      (no workspace: split-KV partials in the library's static per-device array)
   attn_update(lse, go, update_type=1) -> (out, lse_out or None)
   varlen_last_token_gather(x, cu_seqlens) -> x[cu_seqlens[1:] - 1]
   varlen_attn_fwd_workspace_size(...) -> bytes
@@ -38,6 +41,8 @@ __all__ = [
     "status_string",
     "varlen_attn_fwd",
     "varlen_attn_fwd_workspace_size",
+    "varlen_attn_fwd_noalloc",
+    "STATIC_SCRATCH_BYTES",
     "attn_update",
     "varlen_last_token_gather",
     "paged_attn_decode",
@@ -108,6 +113,16 @@ def load_library() -> ctypes.CDLL:
         c.c_float, c.c_int32,                                   # scale causal
         c.c_void_p, c.c_int32, c.c_void_p,                      # out out_dtype lse
         c.c_void_p, c.c_size_t, c.c_void_p,                     # workspace bytes stream
+    ]
+    lib.varlen_attn_fwd_noalloc.restype = c.c_int32
+    lib.varlen_attn_fwd_noalloc.argtypes = [
+        c.c_void_p, c.c_void_p, c.c_void_p, c.c_int32,          # q k v in_dtype
+        c.c_void_p, c.c_void_p,                                 # cu_q cu_k
+        c.c_int32, c.c_int32, c.c_int32, c.c_int32, c.c_int32,  # batch total_q total_k max_q max_k
+        c.c_int32, c.c_int32, c.c_int32,                        # hq hkv d
+        c.c_float, c.c_int32,                                   # scale causal
+        c.c_void_p, c.c_int32, c.c_void_p,                      # out out_dtype lse
+        c.c_void_p,                                             # stream
     ]
     lib.attn_update.restype = c.c_int32
     lib.attn_update.argtypes = [c.c_void_p, c.c_void_p, c.c_int32, c.c_int32, c.c_int64, c.c_int32,
@@ -286,6 +301,46 @@ def varlen_attn_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_
                                     ws_ptr, ws_bytes, _stream_ptr(q.device))
     if st != 0:
         raise VfaError(st, "varlen_attn_fwd_offset")
+    return out, lse
+
+
+STATIC_SCRATCH_BYTES = 16 << 20   # VFA_STATIC_SCRATCH_BYTES in include/vfa.h
+
+
+def varlen_attn_fwd_noalloc(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int, out, lse,
+                            softmax_scale: float | None = None, causal: bool = True):
+    """varlen_attn_fwd for callers that cannot allocate: the caller passes out [Tq,Hq,D] and lse [Tq,Hq]
+    fp32, and the split-KV partials of decode-shaped calls go to the library's static per-device array
+    (STATIC_SCRATCH_BYTES), so nothing is allocated on the call. Calls that need more split-KV storage than
+    the array holds raise VfaError (VFA_ERR_WORKSPACE); calls that overlap on one device race on the array."""
+    torch = _torch()
+    lib = load_library()
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_gpu(name, t, 3, dev)
+    for name, t in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        _check_gpu(name, t, 1, dev)
+        if t.dtype != torch.int32:
+            raise TypeError(f"{name} must be int32")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k and v must share one dtype")
+    if k.shape != v.shape or q.shape[2] != k.shape[2]:
+        raise ValueError("k and v must have one shape, with q's head_dim")
+    tq, hq, d = (int(x) for x in q.shape)
+    tk, hkv = int(k.shape[0]), int(k.shape[1])
+    batch = int(cu_seqlens_q.shape[0]) - 1
+    if int(cu_seqlens_k.shape[0]) != batch + 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+    _check_out("out", out, (tq, hq, d), None, dev)
+    _check_out("lse", lse, (tq, hq), torch.float32, dev)
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    st = lib.varlen_attn_fwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), _dtype_code(q),
+                                     cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(),
+                                     batch, tq, tk, int(max_seqlen_q), int(max_seqlen_k), hq, hkv, d,
+                                     scale, 1 if causal else 0, out.data_ptr(), _dtype_code(out), lse.data_ptr(),
+                                     _stream_ptr(dev))
+    if st != 0:
+        raise VfaError(st, "varlen_attn_fwd_noalloc")
     return out, lse
 
 

@@ -119,7 +119,8 @@ int32_t attn_fwd_impl(const void* q, const void* k, const void* v, int32_t in_dt
                       const int32_t* cu_seqlens_k, const int32_t* causal_offset, int32_t batch, int32_t total_q,
                       int32_t total_k, int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t num_heads_q,
                       int32_t num_heads_kv, int32_t head_dim, float softmax_scale, int32_t causal, void* out,
-                      int32_t out_dtype, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+                      int32_t out_dtype, float* lse, void* workspace, size_t workspace_bytes, void* stream,
+                      bool static_ws = false) {
   if (batch < 0 || total_q < 0 || total_k < 0 || max_seqlen_q < 0 || max_seqlen_k < 0) return VFA_ERR_SHAPE;
   if (batch == 0 || total_q == 0) return VFA_OK;
   if (!q || !k || !v || !cu_seqlens_q || !cu_seqlens_k || !out || !lse) return VFA_ERR_NULL;
@@ -140,10 +141,26 @@ int32_t attn_fwd_impl(const void* q, const void* k, const void* v, int32_t in_dt
   if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return VFA_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return VFA_ERR_UNSUPPORTED;
 
+  const vfa::DecodePlan plan =
+      in_dtype == VFA_BF16
+          ? vfa::plan_decode(batch, total_q, max_seqlen_q, max_seqlen_k, num_heads_q, num_heads_kv, head_dim)
+          : vfa::DecodePlan{false, 0, 0, 0};
+  if (plan.use) {
+    if (static_ws) {
+      if (plan.ws_bytes > vfa::kStaticScratchBytes) return VFA_ERR_WORKSPACE;
+    } else if (!workspace || workspace_bytes < plan.ws_bytes || !aligned16(workspace)) {
+      return VFA_ERR_WORKSPACE;
+    }
+  }
+
   if (debug_checks()) {
     const int r = vfa::check_cu_seqlens(cu_seqlens_q, total_q, max_seqlen_q, cu_seqlens_k, total_k, max_seqlen_k,
                                         batch, stream);
     if (r != 0) return debug_status(r);
+  }
+  if (plan.use && static_ws) {
+    if (vfa::static_scratch(stream, &workspace) != 0) return VFA_ERR_LAUNCH;
+    workspace_bytes = vfa::kStaticScratchBytes;
   }
 
   vfa::AttnArgs a{};
@@ -157,13 +174,7 @@ int32_t attn_fwd_impl(const void* q, const void* k, const void* v, int32_t in_dt
   a.workspace = workspace; a.workspace_bytes = workspace_bytes; a.stream = stream;
 
   if (in_dtype == VFA_F32) return vfa::launch_attn_fwd_f32(a) == 0 ? VFA_OK : VFA_ERR_LAUNCH;
-
-  const vfa::DecodePlan plan =
-      vfa::plan_decode(batch, total_q, max_seqlen_q, max_seqlen_k, num_heads_q, num_heads_kv, head_dim);
-  if (plan.use) {
-    if (!workspace || workspace_bytes < plan.ws_bytes || !aligned16(workspace)) return VFA_ERR_WORKSPACE;
-    return vfa::launch_attn_decode_bf16(a, plan) == 0 ? VFA_OK : VFA_ERR_LAUNCH;
-  }
+  if (plan.use) return vfa::launch_attn_decode_bf16(a, plan) == 0 ? VFA_OK : VFA_ERR_LAUNCH;
   return vfa::launch_attn_fwd_bf16(a) == 0 ? VFA_OK : VFA_ERR_LAUNCH;
 }
 
@@ -191,6 +202,19 @@ VFA_API int32_t varlen_attn_fwd_offset(const void* q, const void* k, const void*
   return attn_fwd_impl(q, k, v, in_dtype, cu_seqlens_q, cu_seqlens_k, causal != 0 ? causal_offset : nullptr,
                        batch, total_q, total_k, max_seqlen_q, max_seqlen_k, num_heads_q, num_heads_kv, head_dim,
                        softmax_scale, causal, out, out_dtype, lse, workspace, workspace_bytes, stream);
+}
+
+static_assert(vfa::kStaticScratchBytes == VFA_STATIC_SCRATCH_BYTES, "static scratch size differs from the header");
+
+VFA_API int32_t varlen_attn_fwd_noalloc(const void* q, const void* k, const void* v, int32_t in_dtype,
+                                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t batch,
+                                        int32_t total_q, int32_t total_k, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                        int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                                        float softmax_scale, int32_t causal, void* out, int32_t out_dtype,
+                                        float* lse, void* stream) {
+  return attn_fwd_impl(q, k, v, in_dtype, cu_seqlens_q, cu_seqlens_k, nullptr, batch, total_q, total_k,
+                       max_seqlen_q, max_seqlen_k, num_heads_q, num_heads_kv, head_dim, softmax_scale, causal, out,
+                       out_dtype, lse, nullptr, 0, stream, true);
 }
 
 VFA_API int32_t attn_update(const float* lse, const void* go, int32_t go_dtype, int32_t sp, int64_t bsh,

@@ -102,6 +102,16 @@ struct GatedDeltaArgs {
   void* stream;
 };
 
+// Size of the library's static per-device scratch array (static_scratch.hip),
+// which holds the split-KV partials of varlen_attn_fwd_noalloc. Equal to
+// VFA_STATIC_SCRATCH_BYTES in include/vfa.h.
+constexpr size_t kStaticScratchBytes = (size_t)16 << 20;
+
+// Device address of that array on the device of `stream`, looked up once per
+// device (hipGetSymbolAddress with the device current) and cached. Returns 0,
+// or -1 on a HIP error.
+int static_scratch(void* stream, void** ptr);
+
 // Each returns 0 on success, -1 if the HIP runtime reported a launch error.
 int launch_attn_fwd_bf16(const AttnArgs& a);
 int launch_attn_decode_bf16(const AttnArgs& a, const DecodePlan& plan);
