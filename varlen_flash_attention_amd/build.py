@@ -26,7 +26,7 @@ LIB = os.path.join(PKG, "libvfa.so")
 
 SOURCES = ["api.cpp", "attn_fwd_bf16.hip", "attn_decode.hip", "attn_fwd_f32.hip", "attn_update.hip",
            "debug_check.hip", "qk_norm_rope.hip", "gated_delta.hip", "gated_delta_chunk.hip",
-           "static_scratch.hip"]
+           "static_scratch.hip", "attn_fwd_overlap.hip"]
 ARCH = "gfx950"
 
 

@@ -27,8 +27,13 @@
 //                   registers.
 // The QK of the next sub-block is issued before the softmax of the current
 // one. K and V stream through LDS in tiles of BN keys with one barrier per
-// tile (see the pipeline comment in the kernel): 128 for the 8-wave shape,
-// 64 for the 4-wave shape, whose two workgroups per CU must share the LDS.
+// tile (see the pipeline comment in the kernel): 64 keys for the 4-wave
+// shape, whose two workgroups per CU share the LDS.
+//
+// This kernel serves batches of short sequences (four waves, 128 columns).
+// Batches whose sequences average at least eight 256-column query tiles go to
+// attn_fwd_overlap.hip, eight waves with the softmax overlapped with the
+// matrix products.
 #include <type_traits>
 
 #include "common.h"
@@ -459,14 +464,12 @@ int launch_w(const AttnArgs& a) {
 
 }  // namespace
 
-// 256-column workgroups once sequences average at least eight of their query
-// tiles (256 / G tokens); shorter ones waste less with 128 columns.
+// 256-column workgroups (attn_fwd_overlap.hip) once sequences average at
+// least eight of their query tiles (256 / G tokens); shorter ones waste less
+// with 128 columns.
 int launch_attn_fwd_bf16(const AttnArgs& a) {
-#if defined(VFA_FORCE_WAVES) && defined(VFA_FORCE_NQ)
-  return launch_w<VFA_FORCE_WAVES, VFA_FORCE_NQ>(a);
-#endif
   const long long mean_q = a.batch > 0 ? (long long)a.total_q / a.batch : 0;
-  if (mean_q >= 8LL * (Shape<8, 1>::COLS / a.grp)) return launch_w<8, 1>(a);
+  if (mean_q >= 8LL * (Shape<8, 1>::COLS / a.grp)) return launch_attn_fwd_overlap(a);
   return launch_w<4, 1>(a);
 }
 

@@ -114,6 +114,8 @@ int static_scratch(void* stream, void** ptr);
 
 // Each returns 0 on success, -1 if the HIP runtime reported a launch error.
 int launch_attn_fwd_bf16(const AttnArgs& a);
+// The 256-column kernel for long sequences (attn_fwd_overlap.hip).
+int launch_attn_fwd_overlap(const AttnArgs& a);
 int launch_attn_decode_bf16(const AttnArgs& a, const DecodePlan& plan);
 int launch_attn_fwd_f32(const AttnArgs& a);
 int launch_paged_decode_bf16(const PagedArgs& a, const PagedPlan& plan);
