@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define VFA_ABI_VERSION 7
+#define VFA_ABI_VERSION 8
 
 typedef enum vfa_status {
   VFA_OK = 0,
@@ -120,7 +120,12 @@ size_t varlen_attn_fwd_workspace_size(int32_t batch, int32_t total_q,
  * lse     [total_q, num_heads_q]              fp32
  * workspace / workspace_bytes: device scratch of at least
  *         varlen_attn_fwd_workspace_size(...) bytes (may be NULL when that
- *         size is 0). Its contents on entry do not matter.
+ *         size is 0). Its contents on entry do not matter. Decode-shaped
+ *         calls keep split-KV partials there; long-sequence prefill (bf16,
+ *         sequences averaging at least 8 * 256 / G query tokens) keeps the
+ *         1 KB of work counters its persistent kernel hands items out with,
+ *         zeroed on the stream before the kernel starts. Calls that run at
+ *         the same time need workspaces of their own.
  * Supported: head_dim 64 or 128; in bf16 -> out bf16 or fp32; in fp32 ->
  *         out fp32. num_heads_q % num_heads_kv == 0 and
  *         num_heads_q / num_heads_kv <= 32.

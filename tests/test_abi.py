@@ -44,7 +44,7 @@ def test_exports_match_header(lib):
 
 
 def test_abi_version(lib):
-    assert lib.vfa_abi_version() == vfa._header_abi_version() == 7
+    assert lib.vfa_abi_version() == vfa._header_abi_version() == 8
 
 
 def test_status_strings(lib):
@@ -202,7 +202,8 @@ def test_workspace_size_plan(lib):
     ws = lib.varlen_attn_fwd_workspace_size
     assert ws(64, 64, 1, 32768, 32, 4, 128) == 8 * 64 * 32 * 129 * 4       # 4096-key splits
     assert ws(2, 2, 1, 4096, 32, 4, 128) == 16 * 2 * 32 * 129 * 4          # 256-key splits for a small batch
-    assert ws(16, 46000, 8192, 8192, 32, 8, 128) == 0                       # prefill
+    assert ws(16, 46000, 8192, 8192, 32, 8, 128) == 1024                    # long prefill: work counters
+    assert ws(64, 18000, 512, 512, 16, 8, 128) == 0                         # short prefill: none
     assert ws(64, 64, 1, 300, 32, 4, 128) == 0                              # short keys: no split
     assert ws(8, 24, 3, 8192, 32, 4, 128) == 0                              # 3 tokens x 8 heads > 16 columns
     assert ws(8, 16, 2, 8192, 16, 2, 64) > 0                                # 2 tokens x 8 heads = 16 columns

@@ -110,7 +110,8 @@ VFA_API size_t varlen_attn_fwd_workspace_size(int32_t batch, int32_t total_q, in
                                               int32_t num_heads_kv, int32_t head_dim) {
   const vfa::DecodePlan p =
       vfa::plan_decode(batch, total_q, max_seqlen_q, max_seqlen_k, num_heads_q, num_heads_kv, head_dim);
-  return p.use ? p.ws_bytes : 0;
+  if (p.use) return p.ws_bytes;
+  return vfa::wide_prefill(batch, total_q, num_heads_q, num_heads_kv) ? vfa::kWidePrefillWorkspace : 0;
 }
 
 namespace {
@@ -141,14 +142,19 @@ int32_t attn_fwd_impl(const void* q, const void* k, const void* v, int32_t in_dt
   if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return VFA_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return VFA_ERR_UNSUPPORTED;
 
+  // bf16 calls take the split-KV (decode) path with its partials workspace,
+  // or, for long sequences, the persistent prefill kernel with its ticket
+  // counters; the fp32 kernel needs no workspace.
   const vfa::DecodePlan plan =
       in_dtype == VFA_BF16
           ? vfa::plan_decode(batch, total_q, max_seqlen_q, max_seqlen_k, num_heads_q, num_heads_kv, head_dim)
           : vfa::DecodePlan{false, 0, 0, 0};
-  if (plan.use) {
+  const bool wide = in_dtype == VFA_BF16 && !plan.use && vfa::wide_prefill(batch, total_q, num_heads_q, num_heads_kv);
+  const size_t ws_need = plan.use ? plan.ws_bytes : (wide ? vfa::kWidePrefillWorkspace : 0);
+  if (ws_need > 0) {
     if (static_ws) {
-      if (plan.ws_bytes > vfa::kStaticScratchBytes) return VFA_ERR_WORKSPACE;
-    } else if (!workspace || workspace_bytes < plan.ws_bytes || !aligned16(workspace)) {
+      if (ws_need > vfa::kStaticScratchBytes) return VFA_ERR_WORKSPACE;
+    } else if (!workspace || workspace_bytes < ws_need || !aligned16(workspace)) {
       return VFA_ERR_WORKSPACE;
     }
   }
@@ -158,7 +164,7 @@ int32_t attn_fwd_impl(const void* q, const void* k, const void* v, int32_t in_dt
                                         batch, stream);
     if (r != 0) return debug_status(r);
   }
-  if (plan.use && static_ws) {
+  if (ws_need > 0 && static_ws) {
     if (vfa::static_scratch(stream, &workspace) != 0) return VFA_ERR_LAUNCH;
     workspace_bytes = vfa::kStaticScratchBytes;
   }

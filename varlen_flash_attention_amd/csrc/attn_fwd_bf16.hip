@@ -468,8 +468,7 @@ int launch_w(const AttnArgs& a) {
 // least eight of their query tiles (256 / G tokens); shorter ones waste less
 // with 128 columns.
 int launch_attn_fwd_bf16(const AttnArgs& a) {
-  const long long mean_q = a.batch > 0 ? (long long)a.total_q / a.batch : 0;
-  if (mean_q >= 8LL * (Shape<8, 1>::COLS / a.grp)) return launch_attn_fwd_overlap(a);
+  if (wide_prefill(a.batch, a.total_q, a.hq, a.hkv)) return launch_attn_fwd_overlap(a);
   return launch_w<4, 1>(a);
 }
 

@@ -10,10 +10,20 @@
 // h / G (core optimisation 5 of the same page), causal mask aligned
 // bottom-right.
 //
-// Work decomposition: one workgroup of 8 waves = one (sequence, kv head, query
-// tile) with 256 query columns (G heads x 256/G tokens), in the XCD-aware block
-// order of the general kernel. Key sub-blocks that the causal mask hides from
-// the whole tile are never visited.
+// Work decomposition: a work item is one (sequence, kv head, query tile) with
+// 256 query columns (G heads x 256/G tokens). Key sub-blocks that the causal
+// mask hides from the whole tile are never visited. The grid is persistent:
+// one workgroup of 8 waves per CU, each taking items one after another from a
+// ticket counter of its XCD (workgroups are dispatched round-robin over the 8
+// XCDs, so workgroup i serves XCD i % 8). XCD x's tickets run over the
+// (sequence, kv head) pairs x, x + 8, ... and, within a pair, its query tiles
+// last first (causal tiles grow with the index), so the items an XCD works on
+// at one time mostly share one pair's K/V in its L2, the longest items start
+// first and a CU that finishes early takes the next item instead of idling.
+// Tickets are slots of a (pair, max_seqlen_q / tokens-per-tile) grid; the
+// first workgroup that draws an empty slot of a pair (a tile past a shorter
+// sequence's end) moves the counter past all of them. The counters sit in the
+// caller's workspace and a one-wave kernel zeroes them before each call.
 //
 // Software pipeline. Per 32-key sub-block a wave runs S_j^T = K_j Q^T (8
 // MFMAs), the online softmax of S_j (exponentials on the transcendental unit,
@@ -29,7 +39,7 @@
 // K and V stream through LDS rings of 4 sub-block slots with one barrier per
 // tile of 2 sub-blocks. Waves 0-3 move K and waves 4-7 move V, one sub-block
 // per iteration: iteration j stores K_{j+3} and V_{j+1} (loaded into registers
-// two iterations earlier) and loads K_{j+5} and V_{j+3}. Iteration j reads K_{j+1}
+// one iteration earlier) and loads K_{j+4} and V_{j+2}. Iteration j reads K_{j+1}
 // and V_{j-1}; a sub-block stored in iteration j is first read in iteration
 // j+2, the next tile, and it replaces one last read in iteration j-2, the
 // previous tile (K_0, read by QK_0 before the first iteration, has a barrier
@@ -50,6 +60,7 @@ constexpr int kThreads = 512;   // 8 waves, two per SIMD
 constexpr int kCols = 256;      // 8 waves x 32 query columns
 constexpr int kSub = 32;        // keys per sub-block
 constexpr int kRing = 4;        // sub-block slots per LDS ring (two tiles of two)
+constexpr int kTicketStride = 32;   // ints between two XCDs' counters (one 128-byte line each)
 
 // LDS row strides as in the general kernel: a 16-byte pad keeps the
 // per-lane-row ds_read_b128 of K conflict-free, a 64-byte pad the transposed
@@ -86,27 +97,71 @@ __device__ __forceinline__ void tile_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// Zeroes the 8 ticket counters (one wave; kernel stores, so a captured graph
+// holds no memset node).
+__global__ void zero_tickets_kernel(int* __restrict__ tickets) {
+  if (threadIdx.x < kXcds) tickets[threadIdx.x * kTicketStride] = 0;
+}
+
+// Next non-empty slot of XCD xcd's ticket range [0, n_slots), or -1 when
+// there is none (run by one thread). A slot whose tile lies past its
+// sequence's end moves the counter to the pair's first non-empty slot. The
+// value drawn grows strictly on every pass, so the loop ends.
+__device__ __forceinline__ int next_slot(int* ctr, int n_slots, int n_mtiles, int xcd, int hkv, int tokw,
+                                      const int32_t* __restrict__ cu_q) {
+  int t = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  while (t < n_slots) {
+    const int pl = t / n_mtiles;
+    const int kk = t - pl * n_mtiles;
+    const int b = (pl * kXcds + xcd) / hkv;
+    const int lq = cu_q[b + 1] - cu_q[b];
+    const int k0 = n_mtiles - min(n_mtiles, max(0, (lq + tokw - 1) / tokw));
+    if (kk >= k0) return t;
+    __hip_atomic_fetch_max(ctr, pl * n_mtiles + k0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    t = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  return -1;
+}
+
 template <int D, bool CAUSAL, typename OutT>
 __global__ __attribute__((amdgpu_flat_work_group_size(1, kThreads), amdgpu_waves_per_eu(2, 2))) void
 attn_fwd_overlap_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
                         const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
                         const int32_t* __restrict__ coff, int batch, int hq, int hkv, int grp, int tokw,
                         int n_mtiles, float scale, float scale_log2, OutT* __restrict__ out,
-                        float* __restrict__ lse) {
+                        float* __restrict__ lse, int* __restrict__ tickets) {
   using S = OverlapSmem<D>;
   constexpr int PT = S::PER_THREAD;
   __shared__ __attribute__((aligned(16))) char smem[S::TOTAL];
+  __shared__ int s_slot;
   char VFA_LDS* kring = (char VFA_LDS*)smem;
   char VFA_LDS* vring = kring + kRing * S::KSLOT;
 
-  // Block -> work: XCD x takes the (sequence, kv head) pairs x, x + 8, ...,
-  // each pair's query tiles back to back, last tile first.
+  // XCD x serves the (sequence, kv head) pairs x, x + 8, ..., n_mtiles slots each.
   const int per_m = batch * hkv;
-  const int id = blockIdx.x;
-  const int xcd = id % kXcds;
-  const int slot = id / kXcds;
+  const int xcd = blockIdx.x % kXcds;
+  const int n_slots = per_m > xcd ? ((per_m - xcd + kXcds - 1) / kXcds) * n_mtiles : 0;
+  int* ctr = tickets + xcd * kTicketStride;
+
+  for (;;) {
+  // The thread index goes through an opaque copy in every item: the per-lane
+  // offsets derived from it are then recomputed per item (a few instructions)
+  // instead of being hoisted out of this loop and held in registers through
+  // the item's own loop.
+  int tid;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(tid) : "v"((int)threadIdx.x));
+  // The barrier after the draw also ends every wave's previous item, so the
+  // new item's stores into the rings follow all reads of the old one.
+  if (tid == 0) s_slot = next_slot(ctr, n_slots, n_mtiles, xcd, hkv, tokw, cu_q);
+  __syncthreads();
+  const int slot = s_slot;
+  if (slot < 0) break;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave (scalar registers)
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int half = lane >> 5;
+  const int group = wave >> 2;                    // 0: waves moving K, 1: waves moving V
   const int bg = (slot / n_mtiles) * kXcds + xcd;
-  if (bg >= per_m) return;
   const int m = n_mtiles - 1 - slot % n_mtiles;
   const int b = bg / hkv;
   const int g = bg % hkv;
@@ -114,18 +169,10 @@ attn_fwd_overlap_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, 
   const int q0 = cu_q[b];
   const int lq = cu_q[b + 1] - q0;
   const int tok_lo = m * tokw;
-  if (tok_lo >= lq) return;
   const int k0 = cu_k[b];
   const int lk = cu_k[b + 1] - k0;
   const int tok_hi = min(lq, tok_lo + tokw);
   const int diag = causal_diag(coff, b, lq, lk);  // query i sees key j iff j <= i + diag (causal)
-
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave (scalar registers)
-  const int lane = tid & 63;
-  const int l32 = lane & 31;
-  const int half = lane >> 5;
-  const int group = wave >> 2;                    // 0: waves moving K, 1: waves moving V
 
   // This lane's query column: (query head of kv head g, token).
   const int col = wave * 32 + l32;
@@ -246,9 +293,21 @@ attn_fwd_overlap_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, 
     ts = (t4[0] + t4[2]) + (t4[1] + t4[3]);
   };
 
-  // One iteration: the softmax of sub-block j (scores in s_cur) between the
-  // MFMAs of QK_{j+1} (into s_next) and PV_{j-1} (with p_prev), plus the
-  // group's staging; then P_j into p_cur. `st` is the staging set that holds
+  // P^T (B operand) for a sub-block's two 16-key steps.
+  auto to_p = [&](const float (&e)[16], bf16x8 (&pp)[2]) VFA_INLINE {
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      bf16x2 pr[4];
+#pragma unroll
+      for (int y = 0; y < 4; ++y) pr[y] = f32x2_to_bf16x2(e[hh * 8 + 2 * y], e[hh * 8 + 2 * y + 1]);
+      pp[hh] = bf16x8{pr[0][0], pr[0][1], pr[1][0], pr[1][1], pr[2][0], pr[2][1], pr[3][0], pr[3][1]};
+    }
+  };
+
+  // One iteration: the softmax of sub-block j (scores in s_cur, P_j into
+  // p_cur) between the MFMAs of QK_{j+1} (into s_next) and PV_{j-1} (with
+  // p_prev), plus the group's staging. A reference move (the slow path)
+  // recomputes P_j. `st` is the staging set that holds
   // sub-block j + ahead.
   auto step = [&](auto do_qk, auto do_pv, int j, f32x16& s_cur, f32x16& s_next, bf16x8 (&p_cur)[2],
                   const bf16x8 (&p_prev)[2], u32x4 (&st)[PT]) VFA_INLINE {
@@ -264,10 +323,12 @@ attn_fwd_overlap_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, 
     float e[16], ts;
     if constexpr (QK && PV) {
       // Sixteen MFMA slots, the order fixed by scheduling barriers between
-      // them. Slot i < 8: the softmax of score i, QK MFMA i, and the two
-      // transposed reads of PV operand i. Slot 8 + i: the softmax of score
-      // 8 + i, the first sum level, and PV MFMA i, whose operand was read 8
-      // slots earlier. The K operands are read up front.
+      // them. Slot i < 8: the probability of score i, QK MFMA i, and the two
+      // transposed reads of PV operand i. Slot 8 + i: the probability of
+      // score 8 + i, its share of the running sum, and PV MFMA i, whose
+      // operand was read 8 slots earlier. Each pair of probabilities becomes
+      // bf16 P as soon as both exist, so few fp32 values stay live. The K
+      // operands are read up front.
       bf16x8 ka[D / 16], va[2][D / 32];
       const char VFA_LDS* krow = kring + ((j + 1) & (kRing - 1)) * S::KSLOT + l32 * S::KSTR + half * 16;
 #pragma unroll
@@ -277,13 +338,20 @@ attn_fwd_overlap_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, 
       constexpr int NQK = D / 16, NPV = 2 * (D / 32);   // 8 and 8 at D = 128, 4 and 4 at D = 64
       constexpr int SPS = 8 / NQK;                       // scores per slot
       static_assert(NQK == NPV && SPS * NQK == 8, "the 16 scores spread evenly over the slots");
-      float t8[8];
+      bf16x2 pr[8];
+      float sum_a = 0.f, sum_b = 0.f;
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < NQK; ++i) {
 #pragma unroll
-        for (int u = 0; u < SPS; ++u)
-          e[i * SPS + u] = fast_exp2(__builtin_fmaf(s_cur[i * SPS + u], scale_log2, -mref));
+        for (int u = 0; u < SPS; ++u) {
+          const int r = i * SPS + u;
+          e[r] = fast_exp2(__builtin_fmaf(s_cur[r], scale_log2, -mref));
+          if (r & 1) {
+            pr[r >> 1] = f32x2_to_bf16x2(e[r - 1], e[r]);
+            sum_a += e[r - 1] + e[r];
+          }
+        }
         s_next = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[i], qreg[i], s_next, 0, 0, 0);
         const int hh = i / (D / 32), db = i % (D / 32);
         const char VFA_LDS* vrow = vb + hh * 16 * S::VSTR;
@@ -294,25 +362,30 @@ attn_fwd_overlap_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, 
       for (int i = 0; i < NPV; ++i) {
 #pragma unroll
         for (int u = 0; u < SPS; ++u) {
-          const int r = i * SPS + u;
-          e[8 + r] = fast_exp2(__builtin_fmaf(s_cur[8 + r], scale_log2, -mref));
-          t8[r] = e[r] + e[8 + r];
+          const int r = 8 + i * SPS + u;
+          e[r] = fast_exp2(__builtin_fmaf(s_cur[r], scale_log2, -mref));
+          if (r & 1) {
+            pr[r >> 1] = f32x2_to_bf16x2(e[r - 1], e[r]);
+            sum_b += e[r - 1] + e[r];
+          }
         }
         const int hh = i / (D / 32), db = i % (D / 32);
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[hh][db], p_prev[hh], acc[db], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
-      float t4[4];
+      ts = sum_a + sum_b;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) t4[r] = t8[r] + t8[r + 4];
-      ts = (t4[0] + t4[2]) + (t4[1] + t4[3]);
+      for (int hh = 0; hh < 2; ++hh)
+        p_cur[hh] = bf16x8{pr[4 * hh][0], pr[4 * hh][1], pr[4 * hh + 1][0], pr[4 * hh + 1][1],
+                           pr[4 * hh + 2][0], pr[4 * hh + 2][1], pr[4 * hh + 3][0], pr[4 * hh + 3][1]};
     } else {
       if constexpr (QK) qk(j + 1, s_next);
       if constexpr (PV) pv(j - 1, p_prev);
       exps(s_cur, e, ts);
+      to_p(e, p_cur);
     }
     sstore(st, j + ahead);
-    gload(st, min(j + ahead + 2, last));
+    gload(st, min(j + ahead + 1, last));
     __builtin_amdgcn_sched_barrier(0);
     const bool slow = !(ts <= kSumLimit) || m_run == neg_inf();
     if (__builtin_amdgcn_ballot_w64(slow)) {
@@ -333,33 +406,25 @@ attn_fwd_overlap_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, 
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
       exps(s_cur, e, ts);
+      to_p(e, p_cur);
     }
     l_run += ts;
-    // P^T (B operand) for the sub-block's two 16-key steps.
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      bf16x2 pr[4];
-#pragma unroll
-      for (int y = 0; y < 4; ++y) pr[y] = f32x2_to_bf16x2(e[hh * 8 + 2 * y], e[hh * 8 + 2 * y + 1]);
-      p_cur[hh] = bf16x8{pr[0][0], pr[0][1], pr[1][0], pr[1][1], pr[2][0], pr[2][1], pr[3][0], pr[3][1]};
-    }
   };
 
   // Prologue: sub-blocks 0-2 of the group's tensor into the ring (the V waves
   // store V_1 and V_2 here and again in iterations 0 and 1, with the same
-  // data, so that both groups run the same loads), then the first two staging
-  // sets in flight.
-  u32x4 st0[PT], st1[PT];
+  // data, so that both groups run the same loads), then the first staged
+  // sub-block in flight.
+  u32x4 st[PT];
   if (n_sub > 0) {
-    u32x4 t2[PT];
-    gload(st0, 0);
-    gload(st1, min(1, last));
+    u32x4 t1[PT], t2[PT];
+    gload(st, 0);
+    gload(t1, min(1, last));
     gload(t2, min(2, last));
-    sstore(st0, 0);
-    sstore(st1, 1);
+    sstore(st, 0);
+    sstore(t1, 1);
     sstore(t2, 2);
-    gload(st0, min(ahead, last));
-    gload(st1, min(ahead + 1, last));
+    gload(st, min(ahead, last));
   }
   tile_barrier();
 
@@ -367,8 +432,7 @@ attn_fwd_overlap_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, 
   using no = std::integral_constant<bool, false>;
   f32x16 sa, sb;
   bf16x8 pa[2], pb[2];
-  // Iteration j uses staging set j & 1 and scores / probabilities a or b by
-  // the parity of j. A tile barrier precedes every even iteration after the
+  // Iteration j uses scores / probabilities a or b by the parity of j. A tile barrier precedes every even iteration after the
   // first, and the final PV when it falls on an even position.
   if (n_sub > 0) {
     // QK_0 reads K_0, whose slot iteration 1 refills with K_4: every wave's
@@ -376,24 +440,24 @@ attn_fwd_overlap_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, 
     qk(0, sa);
     tile_barrier();
     if (n_sub == 1) {
-      step(no{}, no{}, 0, sa, sb, pa, pb, st0);
+      step(no{}, no{}, 0, sa, sb, pa, pb, st);
       pv(0, pa);
     } else {
-      step(yes{}, no{}, 0, sa, sb, pa, pb, st0);
+      step(yes{}, no{}, 0, sa, sb, pa, pb, st);
       int j = 1;
       for (; j + 2 < n_sub; j += 2) {
-        step(yes{}, yes{}, j, sb, sa, pb, pa, st1);
+        step(yes{}, yes{}, j, sb, sa, pb, pa, st);
         tile_barrier();
-        step(yes{}, yes{}, j + 1, sa, sb, pa, pb, st0);
+        step(yes{}, yes{}, j + 1, sa, sb, pa, pb, st);
       }
       if (j == n_sub - 1) {          // last sub-block odd
-        step(no{}, yes{}, j, sb, sa, pb, pa, st1);
+        step(no{}, yes{}, j, sb, sa, pb, pa, st);
         tile_barrier();
         pv(j, pb);
       } else {                       // j == n_sub - 2: last sub-block even
-        step(yes{}, yes{}, j, sb, sa, pb, pa, st1);
+        step(yes{}, yes{}, j, sb, sa, pb, pa, st);
         tile_barrier();
-        step(no{}, yes{}, j + 1, sa, sb, pa, pb, st0);
+        step(no{}, yes{}, j + 1, sa, sb, pa, pb, st);
         pv(j + 1, pa);
       }
     }
@@ -434,6 +498,21 @@ attn_fwd_overlap_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, 
     }
   }
   if (qvalid && half == 0) lse[row] = l_tot > 0.f ? m_run * scale + fast_log2(l_tot) * kLn2 : neg_inf();
+  }
+}
+
+// Persistent grid: one workgroup per CU of the stream's device (a multiple of
+// the 8 XCDs), looked up once per device.
+int persistent_grid(hipStream_t stream) {
+  static int cus[64] = {};
+  hipDevice_t dev = 0;
+  if (hipStreamGetDevice(stream, &dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return -1;
+    cus[dev] = n;
+  }
+  return cus[dev] < kXcds ? kXcds : cus[dev] / kXcds * kXcds;
 }
 
 template <int D, bool CAUSAL, typename OutT>
@@ -441,13 +520,17 @@ int launch_t(const AttnArgs& a) {
   const int tokw = kCols / a.grp;
   const int n_mtiles = (a.max_seqlen_q + tokw - 1) / tokw;
   const long long pairs_per_xcd = ((long long)a.batch * a.hkv + kXcds - 1) / kXcds;
-  const long long blocks = (long long)n_mtiles * pairs_per_xcd * kXcds;
-  if (blocks <= 0) return 0;
-  if (blocks > 0x7fffffffLL) return -1;
-  hipLaunchKernelGGL((attn_fwd_overlap_kernel<D, CAUSAL, OutT>), dim3((unsigned)blocks), dim3(kThreads), 0,
-                     (hipStream_t)a.stream, (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.cu_q, a.cu_k,
-                     a.causal_off, a.batch, a.hq, a.hkv, a.grp, tokw, n_mtiles, a.scale, a.scale * kLog2e,
-                     (OutT*)a.out, a.lse);
+  const long long slots = (long long)n_mtiles * pairs_per_xcd;
+  if (slots <= 0) return 0;
+  if (slots > 0x7fffff00LL) return -1;   // the counters run past the last slot by one draw per workgroup
+  hipStream_t st = (hipStream_t)a.stream;
+  const int grid = persistent_grid(st);
+  if (grid <= 0) return -1;
+  int* tickets = (int*)a.workspace;
+  hipLaunchKernelGGL(zero_tickets_kernel, dim3(1), dim3(64), 0, st, tickets);
+  hipLaunchKernelGGL((attn_fwd_overlap_kernel<D, CAUSAL, OutT>), dim3((unsigned)grid), dim3(kThreads), 0, st,
+                     (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.cu_q, a.cu_k, a.causal_off, a.batch,
+                     a.hq, a.hkv, a.grp, tokw, n_mtiles, a.scale, a.scale * kLog2e, (OutT*)a.out, a.lse, tickets);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

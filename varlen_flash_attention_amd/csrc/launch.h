@@ -26,6 +26,17 @@ struct AttnArgs {
   void* stream;
 };
 
+// Long-sequence prefill: batches whose sequences average at least eight
+// 256-column query tiles (8 * 256 / G tokens, G = hq / hkv) run on the
+// persistent 256-column kernel (attn_fwd_overlap.hip), which takes its work
+// items from ticket counters in a small workspace; shorter ones on the
+// 128-column kernel, which needs none.
+constexpr size_t kWidePrefillWorkspace = 1024;   // 8 XCD counters, one 128-byte line each
+inline bool wide_prefill(int batch, int total_q, int hq, int hkv) {
+  if (batch <= 0 || hq <= 0 || hkv <= 0 || hq % hkv != 0) return false;
+  return (long long)total_q / batch >= 8LL * (256 / (hq / hkv));
+}
+
 // Split-KV plan for short query sets against long key sets (decode).
 struct DecodePlan {
   bool use;          // take the split-KV path
