@@ -16,7 +16,10 @@ RMSNorm + rotary prologue on the long-prefill tokens, the gated delta rule
 (linear attention) on the same lengths and one decode step of it (64
 sequences of one token, state traffic in TB/s), and the attn_update merge of the
 chunked-context config (sp=8, bsh=2048, hd=128, fp32) timed with caches
-flushed before every rep.
+flushed before every rep. The embedding prefill is also timed cold (a 1 GiB
+read before every rep: its 227 MB fit in the last-level cache), and the
+fp64 oracle is timed on full inputs of the tiny, embedding, decode and merge
+configs (`cpu_baseline_per_config`).
 
 "roofline" is the attention kernel's achieved useful FLOP rate (per-launch
 HIP-event durations on the launch stream) against the bf16 dense MFMA peak;
@@ -38,8 +41,8 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_bf16_long_prefill_traffic.json")
-KERNEL_SOURCE = os.path.join(ROOT, "varlen_flash_attention_amd", "csrc", "attn_fwd_bf16.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_long_prefill_traffic.json")
+KERNEL_SOURCE = os.path.join(ROOT, "varlen_flash_attention_amd", "csrc", "attn_fwd_overlap.hip")
 
 
 def log(msg: str) -> None:
@@ -87,7 +90,9 @@ def median(xs):
     return ys[n // 2] if n % 2 else 0.5 * (ys[n // 2 - 1] + ys[n // 2])
 
 
-def attn_case(vfa, torch, w, reps=20, warmup=3, gather=False):
+def attn_case(vfa, torch, w, reps=20, warmup=3, gather=False, cold=False):
+    """One workload's call timed by HIP events; with cold=True each rep follows a 1 GiB read of other
+    data that evicts the inputs from L2 and the 256 MB last-level cache (it leaves them clean)."""
     d = device_inputs(w, torch)
     out = torch.empty((w.total_q, w.num_heads_q, w.head_dim), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((w.total_q, w.num_heads_q), dtype=torch.float32, device="cuda")
@@ -104,6 +109,10 @@ def attn_case(vfa, torch, w, reps=20, warmup=3, gather=False):
 
     ms = time_calls(call, reps, warmup, torch)
     res = attn_stats(w, ms)
+    if cold:
+        scratch = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        res["cold"] = attn_stats(w, time_calls(call, reps, warmup, torch, flush=lambda: scratch.sum()))
+        del scratch
     del d, out, lse, ws, last
     torch.cuda.empty_cache()
     return res
@@ -192,12 +201,13 @@ def prologue_case(vfa, torch, lengths, reps=20, warmup=3):
     return res
 
 
-PEAK_FP32_VECTOR_TFLOPS = 157.3   # MI355X fp32 vector (256 CUs at 2.4 GHz)
-
-
 def gated_delta_case(vfa, torch, lengths, reps=5, warmup=1):
     """gated_delta_rule_fwd on the long-prefill lengths with 16 query/key and 32 value heads, D 128.
-    Algorithmic FLOPs per (token, value head): 7 * Dk * Dv (S^T k, decay, rank-1 write, S^T q)."""
+    Algorithmic FLOPs per (token, value head): 7 * Dk * Dv (S^T k, decay, rank-1 write, S^T q); compulsory
+    bytes: q, k (bf16, shared by 2 value heads), v and out (bf16), g and beta (fp32). Neither HBM nor the
+    matrix unit sets the time: the tokens of a sequence are sequential, and the chunked form runs the
+    longest sequence as a chain of dependent 64-token chunks on one CU, so the time per chain chunk is
+    reported beside the rates."""
     import numpy as np
     from varlen_flash_attention_amd.workloads import bf16_bits, make_gated_delta
 
@@ -218,10 +228,13 @@ def gated_delta_case(vfa, torch, lengths, reps=5, warmup=1):
     t = median(ms)
     tokens = int(p.lengths.sum())
     flops = 7.0 * 128 * 128 * 32 * tokens
+    byt = tokens * (2 * 16 * 128 * 2 + 2 * 32 * 128 * 2 + 2 * 32 * 4)
+    chain = -(-int(p.lengths.max()) // 64)
     res = {"ms_median": round(t, 4), "ms_p10": round(sorted(ms)[len(ms) // 10], 4),
            "ms_p90": round(sorted(ms)[(9 * len(ms)) // 10], 4), "gflop": round(flops / 1e9, 2),
-           "tflops": round(flops / t / 1e9, 2),
-           "frac_fp32_vector_peak": round(flops / t / 1e9 / PEAK_FP32_VECTOR_TFLOPS, 4),
+           "tflops": round(flops / t / 1e9, 2), "compulsory_mb": round(byt / 1e6, 1),
+           "frac_hbm_peak": round(byt / t / 1e6 / PEAK_HBM_GBPS, 4), "bound": "chain of the longest sequence's chunks",
+           "chain_chunks": chain, "us_per_chain_chunk": round(t * 1e3 / chain, 3),
            "tokens": tokens, "longest_sequence": int(p.lengths.max())}
     del q, k, v, g, beta, cu, out
     torch.cuda.empty_cache()
@@ -295,14 +308,20 @@ def merge_case(vfa, torch, reps=100, warmup=5):
     csrc = torch.empty(algo_bytes // 2, dtype=torch.uint8, device="cuda").fill_(7)
     cdst = torch.empty_like(csrc)
     copy_cold = time_calls(lambda: cdst.copy_(csrc), reps, warmup, torch, flush=flush)
+    # Dispatch floors, cold like the merge: a one-element fill (a kernel that
+    # moves nothing) and a read-only sum over the merge's 8.4 MB of partials.
+    tiny = torch.empty(1, dtype=torch.float32, device="cuda")
+    fill_cold = time_calls(lambda: tiny.fill_(1.0), reps, warmup, torch, flush=flush)
+    read_cold = time_calls(lambda: go.sum(), reps, warmup, torch, flush=flush)
     res = {}
-    for name, ms in (("cold", cold), ("warm", warm), ("copy_floor_cold", copy_cold)):
+    for name, ms in (("cold", cold), ("warm", warm), ("copy_floor_cold", copy_cold),
+                     ("one_element_fill_cold", fill_cold), ("read_only_sum_cold", read_cold)):
         t = median(ms)
         res[name] = {"us_median": round(t * 1e3, 3), "gb_per_s": round(algo_bytes / t / 1e6, 1),
                      "frac_hbm_peak": round(algo_bytes / t / 1e6 / PEAK_HBM_GBPS, 4)}
     res["algorithmic_bytes"] = algo_bytes
     res["shape"] = {"sp": sp, "bsh": bsh, "hd": hd, "dtype": "fp32"}
-    del csrc, cdst, go, out, lse, lse_out
+    del csrc, cdst, go, out, lse, lse_out, tiny
     torch.cuda.empty_cache()
 
     # The same kernel on 4x .. 64x the rows, cold: the bandwidth asymptote
@@ -360,6 +379,55 @@ def cpu_baseline(w, budget_s=12.0):
                       f"{len(os.sched_getaffinity(0))} usable cores"}
 
 
+def cpu_baselines():
+    """The fp64 oracle on the other configs: full inputs of the tiny fp32 config, the embedding prefill
+    with its gather and the chunked-context merge, and two of the decode config's 64 sequences (the
+    long-prefill oracle is the sampled `cpu_baseline`). Each is timed once with time.perf_counter on the host's BLAS threads and
+    reported on the same useful-FLOP (or algorithmic-byte) count as the GPU."""
+    import numpy as np
+    import oracle
+    from varlen_flash_attention_amd.workloads import make_workload
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    res = {"cores": len(os.sched_getaffinity(0)), "blas_threads": threads, "kind": "oracle"}
+    for name in ("tiny_fp32", "embed_prefill"):
+        w = make_workload(name)
+        t0 = time.perf_counter()
+        o, _ = oracle.varlen_attention(w.q, w.k, w.v, w.cu_seqlens_q, w.cu_seqlens_k, w.num_heads_kv, w.scale,
+                                       w.causal)
+        if name == "embed_prefill":
+            oracle.last_token_gather(o, w.cu_seqlens_q)
+        el = time.perf_counter() - t0
+        res[name] = {"s": round(el, 3), "useful_gflop": round(w.useful_flops() / 1e9, 3),
+                     "useful_tflops": round(w.useful_flops() / el / 1e12, 6), "sample": "full inputs"}
+    # Decode: the oracle walks each (sequence, head) over strided K/V rows, minutes for all 64 sequences,
+    # so it runs on the first two sequences of the same workload (same values) and reports that rate.
+    w = make_workload("decode")
+    ck = w.cu_seqlens_k.astype(np.int64)
+    sub = 2
+    cu_q = w.cu_seqlens_q[:sub + 1]
+    cu_k = w.cu_seqlens_k[:sub + 1]
+    t0 = time.perf_counter()
+    oracle.varlen_attention(w.q[:sub], w.k[:ck[sub]], w.v[:ck[sub]], cu_q, cu_k, w.num_heads_kv, w.scale, w.causal)
+    el = time.perf_counter() - t0
+    fl = 4.0 * w.head_dim * w.num_heads_q * float(ck[sub])
+    res["decode"] = {"s": round(el, 3), "useful_gflop": round(fl / 1e9, 3), "useful_tflops": round(fl / el / 1e12, 6),
+                     "sample": f"sequences 0-{sub - 1} of {w.batch} ({int(ck[sub])} of {w.total_k} keys)"}
+    rng = np.random.default_rng(5)
+    sp, bsh, hd = 8, 64 * 32, 128
+    lse = rng.normal(8.0, 2.0, (sp, bsh)).astype(np.float32)
+    go = rng.standard_normal((sp, bsh, hd)).astype(np.float32)
+    t0 = time.perf_counter()
+    oracle.attn_update(lse, go, 1)
+    el = time.perf_counter() - t0
+    nbytes = sp * bsh * (hd + 1) * 4 + bsh * (hd + 1) * 4
+    res["merge"] = {"s": round(el, 4), "algorithmic_bytes": nbytes, "gb_per_s": round(nbytes / el / 1e9, 3)}
+    return res
+
+
 def traffic_record():
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it matches the kernel source."""
     try:
@@ -404,10 +472,13 @@ def main() -> int:
     d = device_inputs(w, torch)
     out = torch.empty((w.total_q, w.num_heads_q, w.head_dim), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((w.total_q, w.num_heads_q), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(1, vfa.varlen_attn_fwd_workspace_size(w.batch, w.total_q, w.max_seqlen_q, w.max_seqlen_k,
+                                                                w.num_heads_q, w.num_heads_kv, w.head_dim)),
+                     dtype=torch.uint8, device="cuda")
 
     def step():
         vfa.varlen_attn_fwd(d["q"], d["k"], d["v"], d["cu_q"], d["cu_k"], w.max_seqlen_q, w.max_seqlen_k,
-                            softmax_scale=w.scale, causal=True, out=out, lse=lse)
+                            softmax_scale=w.scale, causal=True, out=out, lse=lse, workspace=ws)
 
     for _ in range(args.warmup):
         step()
@@ -430,7 +501,7 @@ def main() -> int:
     achieved = flops / (avg_launch * 1e-3) / 1e12
     log(f"[bench] {args.steps} steps in {wall * 1e3:.1f} ms; avg launch {avg_launch:.3f} ms; "
         f"{achieved:.1f} TFLOP/s useful")
-    del d, out, lse
+    del d, out, lse, ws
     torch.cuda.empty_cache()
 
     if args.copy_calibration:
@@ -446,7 +517,8 @@ def main() -> int:
     extra = {}
     if not args.no_extra:
         log("[bench] extra: embed_prefill")
-        extra["embed_prefill_with_gather"] = attn_case(vfa, torch, make_workload("embed_prefill"), gather=True)
+        extra["embed_prefill_with_gather"] = attn_case(vfa, torch, make_workload("embed_prefill"), gather=True,
+                                                       cold=True)
         log("[bench] extra: long_prefill non-causal")
         extra["long_prefill_full"] = attn_case(vfa, torch, make_workload("long_prefill_full"))
         log("[bench] extra: decode")
@@ -469,6 +541,8 @@ def main() -> int:
     if not args.no_cpu:
         log("[bench] cpu baseline (oracle)")
         cpu = cpu_baseline(w)
+        log("[bench] cpu baselines of the other configs, full inputs")
+        extra["cpu_baseline_per_config"] = cpu_baselines()
 
     result = {
         "metric": "varlen attn useful TFLOP/s (% bf16 MFMA peak)",

@@ -140,7 +140,8 @@ def test_bench_refuses_more_than_one_gpu():
 
 # ------------------------------------------------------------------ rocprofv3 summariser
 
-HEAD = "_ZN3vfa12_GLOBAL__N_120attn_fwd_bf16_kernelILi8ELi1ELi128ELb1EDF16bEEvX"
+HEAD = "_ZN3vfa12_GLOBAL__N_123attn_fwd_overlap_kernelILi128ELb1EDF16bEEvX"
+EMBED = "_ZN3vfa12_GLOBAL__N_120attn_fwd_bf16_kernelILi4ELi1ELi128ELb1EDF16bLi64EEEvX"
 
 
 def _write_csv(path, header, rows):
@@ -156,7 +157,8 @@ def test_profile_summary_on_synthetic_counters(tmp_path):
     src, dst = tmp_path / "prof", tmp_path / "out"
     steps, warmup = 3, 2
     bench = {"steps": steps, "warmup": warmup, "config": {"useful_gflop_per_step": 2000.0},
-             "roofline": {"achieved": 1000.0, "frac": 0.4}}
+             "roofline": {"achieved": 1000.0, "frac": 0.4},
+             "extra": {"embed_prefill_with_gather": {"useful_gflop": 20.0}}}
     os.makedirs(src, exist_ok=True)
     (src / "trace.log").write_text("[bench] noise\n" + json.dumps(bench) + "\n")
     # 5 launches of the headline kernel, 1000 ns apart, durations 2.0 .. 2.4 ms
@@ -172,13 +174,27 @@ def test_profile_summary_on_synthetic_counters(tmp_path):
                    ["Kernel_Name", "Counter_Name", "Counter_Value"],
                    [["__amd_rocclr_copyBuffer", counter, copy_val], [HEAD, counter, head_val],
                     [HEAD, counter, head_val]])
+    # MFMA counters: one dispatch of the headline kernel, 2 ms long, 8 XCCs x 3.6M active cycles (1.8 GHz);
+    # 2100 GFLOP issued (4.1016e9 MOPS x 512) and busy cycles for 50% of 1024 SIMDs
+    mf = []
+    for name, val in (("SQ_INSTS_VALU_MFMA_MOPS_BF16", 2100e9 / 512), ("SQ_VALU_MFMA_BUSY_CYCLES", 0.5 * 1024 * 3.6e6),
+                      ("SQ_INSTS_MFMA", 64e6), ("SQ_INSTS_VALU", 256e6), ("SQ_BUSY_CU_CYCLES", 1.0),
+                      ("GRBM_GUI_ACTIVE", 8 * 3.6e6)):
+        mf.append([7, HEAD, name, val, 0, 2_000_000])
+    _write_csv(str(src / "MFMA" / "bench_counter_collection.csv"),
+               ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"], mf)
     profile_summary.main(str(src), str(dst))
-    rec = json.load(open(dst / "attn_fwd_bf16_long_prefill_traffic.json"))
+    mtxt = (dst / "prefill_kernels.mfma_counters.txt").read_text()
+    assert "clock 1.80 GHz" in mtxt
+    assert "issued MFMA 2100.0 GFLOP vs useful 2000.0 GFLOP: 1.050x" in mtxt
+    assert "MFMA busy per SIMD 0.500" in mtxt
+    assert "4.00 VALU per MFMA" in mtxt
+    rec = json.load(open(dst / "attn_fwd_long_prefill_traffic.json"))
     assert rec["copy_calibration"]["fetch_scale"] == pytest.approx(2.0)
     assert rec["copy_calibration"]["write_scale"] == pytest.approx(1.0)
     assert rec["hbm_read_bytes_per_launch"] == 2 * 1000 * 1024
     assert rec["hbm_write_bytes_per_launch"] == 500 * 1024
-    txt = (dst / "attn_fwd_bf16_long_prefill.kernel_stats.txt").read_text()
+    txt = (dst / "attn_fwd_long_prefill.kernel_stats.txt").read_text()
     # timed launches are dispatches 2, 3, 4 (after 2 warm-up): 2.2, 2.3, 2.4 ms -> 2300 us
     assert "average 2300.0 us" in txt
     assert f"gave {2000.0 / 1000.0 * 1e3:.1f} us" in txt
