@@ -30,9 +30,29 @@ def declared_functions():
 
 @pytest.fixture(scope="module")
 def lib():
-    if not os.path.exists(vfa.library_path()):
+    # test_host_sanitizer.py runs this file against a build of the C-ABI layer
+    # with sanitizers and stub launchers, named by VFA_TEST_LIBRARY.
+    alt = os.environ.get("VFA_TEST_LIBRARY")
+    if alt:
+        vfa._LIB = None
+        vfa.library_path = lambda: alt
+    elif not os.path.exists(vfa.library_path()):
         vbuild.build()
     return vfa.load_library()
+
+
+@pytest.fixture(autouse=True)
+def no_launch(request):
+    """With the stub build, no call in this file may reach a launcher or a device check."""
+    if "lib" not in request.fixturenames:
+        yield
+        return
+    lib = request.getfixturevalue("lib")
+    count = getattr(lib, "vfa_stub_launch_count", None)
+    before = count() if count else 0
+    yield
+    if count:
+        assert count() == before, "a call reached the GPU side"
 
 
 def test_exports_match_header(lib):

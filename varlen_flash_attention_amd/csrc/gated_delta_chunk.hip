@@ -43,7 +43,7 @@
 namespace vfa {
 namespace {
 
-constexpr int kC = 64;                  // tokens per chunk
+constexpr int kC = kGdnChunk;          // tokens per chunk
 
 typedef __attribute__((__vector_size__(2 * sizeof(double)))) double f64x2;
 
@@ -788,11 +788,8 @@ int launch_t(const GatedDeltaArgs& a, int n_chunks, bf16* wt, bf16* wm, float* w
 
 // Up to this many sequences are ranked by length for the chunk kernel; larger
 // batches keep their own order. The ranking costs O(batch) per sequence.
-constexpr int kOrderMax = 4096;
-
-size_t gated_delta_chunk_workspace(long long tokens, int hv) {
-  return (size_t)tokens * hv * (2 * 2 * kC * sizeof(bf16) + 2 * sizeof(float)) + kOrderMax * sizeof(int32_t);
-}
+constexpr int kOrderMax = kGdnOrderMax;
+static_assert(sizeof(bf16) == 2, "the workspace size in launch.h counts bf16 as 2 bytes");
 
 int launch_gated_delta_chunked(const GatedDeltaArgs& a, int max_seqlen, void* workspace) {
   if (a.batch <= 0 || max_seqlen <= 0 || a.tokens <= 0) return 0;

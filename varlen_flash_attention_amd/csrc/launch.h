@@ -134,9 +134,17 @@ int launch_attn_update(const float* lse, const void* go, int go_dtype, int sp, i
                        int update_type, void* out, float* lse_out, void* stream);
 int launch_qk_norm_rope(const QkNormRopeArgs& a);
 int launch_gated_delta(const GatedDeltaArgs& a);
-// Chunked form (gated_delta_chunk.hip): bytes of workspace for `tokens` packed
-// tokens and hv value heads, and the two-kernel launch using it.
-size_t gated_delta_chunk_workspace(long long tokens, int hv);
+// Chunked form (gated_delta_chunk.hip): tokens per chunk; sequences ranked by
+// length for the chunk kernel's order (larger batches keep their own order);
+// bytes of workspace for `tokens` packed tokens and hv value heads (per token
+// and value head, T and M as bf16 hi/lo rows of kGdnChunk, 2 bytes each, and
+// two fp32 decay factors; then a fixed slot of kGdnOrderMax int32 for the
+// order); and the two-kernel launch using it.
+constexpr int kGdnChunk = 64;
+constexpr int kGdnOrderMax = 4096;
+inline size_t gated_delta_chunk_workspace(long long tokens, int hv) {
+  return (size_t)tokens * hv * (2 * 2 * kGdnChunk * 2 + 2 * sizeof(float)) + kGdnOrderMax * sizeof(int32_t);
+}
 int launch_gated_delta_chunked(const GatedDeltaArgs& a, int max_seqlen, void* workspace);
 int launch_last_token_gather(const void* x, int esize, const int32_t* cu, int batch, int64_t row_elems,
                              void* out, void* stream);
