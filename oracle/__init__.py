@@ -29,7 +29,10 @@ Parity status per function (what pins it; see tests/test_oracle_*.py):
       (tests/golden/gated_delta_handworked.json), beta = 0 closed form,
       orthonormal-key associative recall, continuation through the state,
       packed == per sequence, linearity in v, and an independently written
-      chunked (WY) formulation.
+      chunked (WY) formulation. These pin it to the recurrence its docstring
+      states; the page that names the operator prints no formula, so that
+      recurrence is a reading and its agreement with the page's own operator
+      is unpinned.
 """
 from .attention import (  # noqa: F401
     varlen_attention,
