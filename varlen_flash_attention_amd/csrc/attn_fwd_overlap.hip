@@ -339,7 +339,7 @@ attn_fwd_overlap_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, 
       constexpr int SPS = 8 / NQK;                       // scores per slot
       static_assert(NQK == NPV && SPS * NQK == 8, "the 16 scores spread evenly over the slots");
       bf16x2 pr[8];
-      float sum_a = 0.f, sum_b = 0.f;
+      float sum_a, sum_b;   // each starts at its first pair's sum (no add of zero)
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < NQK; ++i) {
@@ -349,7 +349,7 @@ attn_fwd_overlap_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, 
           e[r] = fast_exp2(__builtin_fmaf(s_cur[r], scale_log2, -mref));
           if (r & 1) {
             pr[r >> 1] = f32x2_to_bf16x2(e[r - 1], e[r]);
-            sum_a += e[r - 1] + e[r];
+            sum_a = r == 1 ? e[0] + e[1] : sum_a + (e[r - 1] + e[r]);
           }
         }
         s_next = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[i], qreg[i], s_next, 0, 0, 0);
@@ -366,7 +366,7 @@ attn_fwd_overlap_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, 
           e[r] = fast_exp2(__builtin_fmaf(s_cur[r], scale_log2, -mref));
           if (r & 1) {
             pr[r >> 1] = f32x2_to_bf16x2(e[r - 1], e[r]);
-            sum_b += e[r - 1] + e[r];
+            sum_b = r == 9 ? e[8] + e[9] : sum_b + (e[r - 1] + e[r]);
           }
         }
         const int hh = i / (D / 32), db = i % (D / 32);
