@@ -141,7 +141,7 @@ def test_bench_refuses_more_than_one_gpu():
 # ------------------------------------------------------------------ rocprofv3 summariser
 
 HEAD = "_ZN3vfa12_GLOBAL__N_123attn_fwd_overlap_kernelILi128ELb1EDF16bEEvX"
-EMBED = "_ZN3vfa12_GLOBAL__N_120attn_fwd_bf16_kernelILi4ELi1ELi128ELb1EDF16bLi64EEEvX"
+EMBED = "_ZN3vfa12_GLOBAL__N_121attn_fwd_short_kernelILi128ELb1EDF16bEEvX"
 
 
 def _write_csv(path, header, rows):

@@ -22,7 +22,7 @@ MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS
 MFMA_CMD = ("cd /tmp && rocprofv3 --pmc " + MFMA_COUNTERS + " --output-format csv -d <dir>/MFMA -o bench -- "
             "python3 <repo>/bench.py --no-cpu --steps 3 --warmup 1")
 HEAD = "attn_fwd_overlap_kernelILi128ELb1EDF16b"   # the long-prefill kernel: D=128, causal, bf16 out
-EMBED = "attn_fwd_bf16_kernelILi4ELi1ELi128ELb1EDF16b"   # 4 waves x 32 columns, D=128, causal, bf16 out
+EMBED = "attn_fwd_short_kernelILi128ELb1EDF16b"   # short sequences: D=128, causal, bf16 out
 SIMDS = 1024          # MI355X: 256 CUs x 4 SIMDs
 XCCS = 8
 MERGE = "attn_update_kernel<float, 128, 8, 1>"          # the merge config shape (one row per thread)
@@ -62,7 +62,7 @@ def main(src, dst):
     lines += ["",
               "kernel name key: attn_fwd_overlap_kernel<D, CAUSAL, OutT> (ILi128ELb1 = D 128, causal: the headline; "
               "ILi128ELb0 = the non-causal extra) runs after zero_tickets_kernel, which clears its work counters; "
-              "attn_fwd_bf16_kernel<WAVES, NQ, D, CAUSAL, OutT, BN> with ILi4ELi1 = 4 waves of 32 query columns "
+              "attn_fwd_short_kernel<D, CAUSAL, OutT> (4 waves of 32 query columns, three workgroups per CU) "
               "serves the embedding prefill.",
               "  attn_decode_split_kernel<D, CAUSAL, PAGED, OutT>: ILi128ELb1ELb0 = contiguous decode (bench extra "
               "'decode'), ILi128ELb1ELb1 = paged decode (extras 'paged_decode_p16' and '_p128', one row for both).",
