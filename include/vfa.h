@@ -122,10 +122,13 @@ size_t varlen_attn_fwd_workspace_size(int32_t batch, int32_t total_q,
  *         varlen_attn_fwd_workspace_size(...) bytes (may be NULL when that
  *         size is 0). Its contents on entry do not matter. Decode-shaped
  *         calls keep split-KV partials there; long-sequence prefill (bf16,
- *         sequences averaging at least 8 * 256 / G query tokens) keeps the
- *         1 KB of work counters its persistent kernel hands items out with,
- *         zeroed on the stream before the kernel starts. Calls that run at
- *         the same time need workspaces of their own.
+ *         sequences averaging at least 8 * 256 / G query tokens, and
+ *         (max_seqlen_k + 256) * num_heads_kv * head_dim * 2 < 2^32, i.e. one
+ *         sequence's keys short of 4 GiB) keeps the 1 KB of work counters its
+ *         persistent kernel hands items out with, zeroed on the stream before
+ *         the kernel starts. Longer key sets run on the kernel that needs no
+ *         workspace. Calls that run at the same time need workspaces of their
+ *         own.
  * Supported: head_dim 64 or 128; in bf16 -> out bf16 or fp32; in fp32 ->
  *         out fp32. num_heads_q % num_heads_kv == 0 and
  *         num_heads_q / num_heads_kv <= 32.

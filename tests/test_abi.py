@@ -223,6 +223,11 @@ def test_workspace_size_plan(lib):
     assert ws(64, 64, 1, 32768, 32, 4, 128) == 8 * 64 * 32 * 129 * 4       # 4096-key splits
     assert ws(2, 2, 1, 4096, 32, 4, 128) == 16 * 2 * 32 * 129 * 4          # 256-key splits for a small batch
     assert ws(16, 46000, 8192, 8192, 32, 8, 128) == 1024                    # long prefill: work counters
+    # The persistent kernel needs (max_seqlen_k + 256) * Hkv * D * 2 bytes of keys below 2^32; past that the
+    # sequence runs on the kernel without counters.
+    assert ws(1, 8192, 8192, 2**32 // 2048 - 257, 64, 8, 128) == 1024
+    assert ws(1, 8192, 8192, 2**32 // 2048 - 256, 64, 8, 128) == 0
+    assert ws(2, 812, 512, 2_100_001, 64, 8, 128) == 0
     assert ws(64, 18000, 512, 512, 16, 8, 128) == 0                         # short prefill: none
     assert ws(64, 64, 1, 300, 32, 4, 128) == 0                              # short keys: no split
     assert ws(8, 24, 3, 8192, 32, 4, 128) == 0                              # 3 tokens x 8 heads > 16 columns

@@ -111,7 +111,8 @@ VFA_API size_t varlen_attn_fwd_workspace_size(int32_t batch, int32_t total_q, in
   const vfa::DecodePlan p =
       vfa::plan_decode(batch, total_q, max_seqlen_q, max_seqlen_k, num_heads_q, num_heads_kv, head_dim);
   if (p.use) return p.ws_bytes;
-  return vfa::wide_prefill(batch, total_q, num_heads_q, num_heads_kv) ? vfa::kWidePrefillWorkspace : 0;
+  const bool wide = vfa::wide_prefill(batch, total_q, max_seqlen_k, num_heads_q, num_heads_kv, head_dim);
+  return wide ? vfa::kWidePrefillWorkspace : 0;
 }
 
 namespace {
@@ -149,7 +150,8 @@ int32_t attn_fwd_impl(const void* q, const void* k, const void* v, int32_t in_dt
       in_dtype == VFA_BF16
           ? vfa::plan_decode(batch, total_q, max_seqlen_q, max_seqlen_k, num_heads_q, num_heads_kv, head_dim)
           : vfa::DecodePlan{false, 0, 0, 0};
-  const bool wide = in_dtype == VFA_BF16 && !plan.use && vfa::wide_prefill(batch, total_q, num_heads_q, num_heads_kv);
+  const bool wide = in_dtype == VFA_BF16 && !plan.use &&
+                    vfa::wide_prefill(batch, total_q, max_seqlen_k, num_heads_q, num_heads_kv, head_dim);
   const size_t ws_need = plan.use ? plan.ws_bytes : (wide ? vfa::kWidePrefillWorkspace : 0);
   if (ws_need > 0) {
     if (static_ws) {

@@ -134,26 +134,33 @@ attn_fwd_short_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, co
   int j_full = lk / 32;
   if (CAUSAL) j_full = min(j_full, max(0, (tok_lo + diag + 1) / 32));
 
-  // Global-to-LDS loads. The sequence's rows of kv head g form one buffer
-  // whose size ends at its last key, so rows past the end read as zero (those
-  // keys are masked). Wave w moves lines w * PW .. w * PW + PW - 1 of a
-  // sub-block of K and of V; lane L brings 4 bytes of key row
-  // L / (64 / RPD) of the line, the row offset of each line going to the
-  // scalar offset and its LDS address to M0.
+  // Global-to-LDS loads. Each call makes one buffer per tensor over the 32
+  // key rows of kv head g in the sub-block, its size ending at the sequence's
+  // last key, so rows past the end read as zero (those keys are masked).
+  // Rebasing per sub-block keeps every byte offset below 32 rows whatever the
+  // sequence length. Wave w moves lines w * PW .. w * PW + PW - 1 of K and of
+  // V; lane L brings 4 bytes of key row L / (64 / RPD) of the line, the row
+  // offset of each line going to the scalar offset and its LDS address to M0.
   const uint32_t row_bytes = (uint32_t)hkv * D * sizeof(bf16);
-  const uint32_t nrec = (uint32_t)lk * row_bytes;
-  const __amdgpu_buffer_rsrc_t krsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(k + ((size_t)k0 * hkv + g) * D), (short)0, (int)nrec, 0x00020000);
-  const __amdgpu_buffer_rsrc_t vrsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(v + ((size_t)k0 * hkv + g) * D), (short)0, (int)nrec, 0x00020000);
+  const size_t sub_elems = (size_t)32 * hkv * D;
+  const bf16* kseq = k + ((size_t)k0 * hkv + g) * D;
+  const bf16* vseq = v + ((size_t)k0 * hkv + g) * D;
   const uint32_t l_voff = (uint32_t)(lane / (64 / S::RPD)) * row_bytes + (uint32_t)(lane % (64 / S::RPD)) * 4u;
+  const uint32_t w_soff = (uint32_t)wave * S::PW * S::RPD * row_bytes;
   auto dma = [&](int sub, int bsel) VFA_INLINE {
+    // readfirstlane keeps the (uniform) size in an SGPR: a size the compiler
+    // leaves in a VGPR would make it loop over lanes for every load.
+    const uint32_t nrec =
+        (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)min(max(lk - sub * 32, 0), 32) * row_bytes));
+    const __amdgpu_buffer_rsrc_t krsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(kseq + sub * sub_elems), (short)0, (int)nrec, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vrsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(vseq + sub * sub_elems), (short)0, (int)nrec, 0x00020000);
     char VFA_LDS* kd = kbuf + bsel * S::KBUF + wave * S::PW * S::KLSTR;
     char VFA_LDS* vd = vbuf + bsel * S::VBUF + wave * S::PW * S::VLSTR;
-    const uint32_t soff = ((uint32_t)sub * 32 + (uint32_t)wave * S::PW * S::RPD) * row_bytes;
 #pragma unroll
     for (int i = 0; i < S::PW; ++i) {
-      const uint32_t so = soff + (uint32_t)(i * S::RPD) * row_bytes;
+      const uint32_t so = w_soff + (uint32_t)(i * S::RPD) * row_bytes;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(krsrc, (VFA_LDS void*)(kd + i * S::KLSTR), 4, l_voff, so, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(vrsrc, (VFA_LDS void*)(vd + i * S::VLSTR), 4, l_voff, so, 0, 0);
     }
@@ -324,7 +331,7 @@ int launch_short(const AttnArgs& a) {
 }  // namespace
 
 int launch_attn_fwd_bf16(const AttnArgs& a) {
-  if (wide_prefill(a.batch, a.total_q, a.hq, a.hkv)) return launch_attn_fwd_overlap(a);
+  if (wide_prefill(a.batch, a.total_q, a.max_seqlen_k, a.hq, a.hkv, a.head_dim)) return launch_attn_fwd_overlap(a);
   const bool f32out = a.out_dtype == 0;
   if (a.head_dim == 128) {
     if (a.causal) return f32out ? launch_short<128, true, float>(a) : launch_short<128, true, bf16>(a);

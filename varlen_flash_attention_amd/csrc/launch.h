@@ -30,10 +30,14 @@ struct AttnArgs {
 // 256-column query tiles (8 * 256 / G tokens, G = hq / hkv) run on the
 // persistent 256-column kernel (attn_fwd_overlap.hip), which takes its work
 // items from ticket counters in a small workspace; shorter ones on the
-// 128-column kernel, which needs none.
+// 128-column kernel, which needs none. The persistent kernel addresses all
+// keys of a sequence and kv head through one buffer with 32-bit byte offsets,
+// so a sequence whose keys span 4 GiB or more (with a 256-row margin for the
+// last sub-block) goes to the 128-column kernel, which rebases per sub-block.
 constexpr size_t kWidePrefillWorkspace = 1024;   // 8 XCD counters, one 128-byte line each
-inline bool wide_prefill(int batch, int total_q, int hq, int hkv) {
-  if (batch <= 0 || hq <= 0 || hkv <= 0 || hq % hkv != 0) return false;
+inline bool wide_prefill(int batch, int total_q, int max_seqlen_k, int hq, int hkv, int head_dim) {
+  if (batch <= 0 || hq <= 0 || hkv <= 0 || hq % hkv != 0 || max_seqlen_k < 0 || head_dim <= 0) return false;
+  if (((long long)max_seqlen_k + 256) * hkv * head_dim * 2 >= (1LL << 32)) return false;
   return (long long)total_q / batch >= 8LL * (256 / (hq / hkv));
 }
 
