@@ -189,8 +189,6 @@ attn_fwd_short_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, co
   const int v_lane = S::vrow(tr_key) + tr_d * 2;
 
   f32x16 acc[D / 32];
-#pragma unroll
-  for (int i = 0; i < D / 32; ++i) acc[i] = f32x16{};
   // Per column: reference max m_run (raw score units; -inf until the column
   // has seen a visible key), the same pre-scaled to log2 units, and the
   // running sum of probabilities against it. The reference only has to keep
@@ -201,9 +199,11 @@ attn_fwd_short_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, co
   float m_run = neg_inf(), mref = 0.f, l_run = 0.f;
   constexpr float kSumLimit = 4294967296.f;
 
-  // Sub-block 0 (and Q) landed in every wave, then the workgroup barrier.
-  asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  for (int j = 0; j < n_sub; ++j) {
+  // One 32-key sub-block. The first has no history: its exact max becomes
+  // the reference directly (O and the sum are zero, so nothing is rescaled)
+  // and its PV products start O.
+  auto sub_block = [&](int j, auto first_c) VFA_INLINE {
+    constexpr bool FIRST = decltype(first_c)::value;
     const int bsel = j & 1;
     // The other buffer held sub-block j - 1, which every wave finished before
     // the barrier that ended iteration j - 1.
@@ -214,11 +214,11 @@ attn_fwd_short_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, co
     for (int ks = 0; ks < D / 16; ++ks)
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read_b128(krow + ks * 32), qreg[ks], s, 0, 0, 0);
     if (j >= j_full) {
-      const int lim = CAUSAL ? min(lk - 1, tq + diag) : lk - 1;
-      const int kb0 = j * 32 + half * 4;
+      // Keys past the row's last visible one, as offsets from this lane's first key.
+      const int rel = (CAUSAL ? min(lk - 1, tq + diag) : lk - 1) - (j * 32 + half * 4);
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        if (kb0 + (r >> 2) * 8 + (r & 3) > lim) s[r] = neg_inf();
+        if ((r >> 2) * 8 + (r & 3) > rel) s[r] = neg_inf();
     }
     // Probabilities against the current reference and their fp32 sum (of the
     // unrounded values, so lse stays fp32-accurate), summed as a tree.
@@ -233,27 +233,38 @@ attn_fwd_short_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, co
       for (int r = 0; r < 4; ++r) t4[r] = t8[r] + t8[r + 4];
       ts = (t4[0] + t4[2]) + (t4[1] + t4[3]);
     };
-    exps();
-    if (__builtin_amdgcn_ballot_w64(!(ts <= kSumLimit) || m_run == neg_inf())) {
+    // The sub-block's exact max per column; the other lane half holds the
+    // other keys of the same column.
+    auto block_max = [&]() VFA_INLINE {
       float x = neg_inf();
 #pragma unroll
       for (int r = 0; r < 16; ++r) x = fmaxf(x, s[r]);
-      // The other lane half holds the other keys of the same column.
       auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-      const float m_new = fmaxf(m_run, fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])));
-      // Unchanged references scale by exactly 1 (m_run may be -inf); one moving
-      // up from -inf scales the (zero) history by 0.
-      const float alpha = m_new == m_run ? 1.f : fast_exp2((m_run - m_new) * scale_log2);
-      m_run = m_new;
-      mref = m_new == neg_inf() ? 0.f : m_new * scale_log2;
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+      return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    };
+    if constexpr (FIRST) {
+      m_run = block_max();
+      mref = m_run == neg_inf() ? 0.f : m_run * scale_log2;
       exps();
+      l_run = ts;
+    } else {
+      exps();
+      if (__builtin_amdgcn_ballot_w64(!(ts <= kSumLimit) || m_run == neg_inf())) {
+        const float m_new = fmaxf(m_run, block_max());
+        // Unchanged references scale by exactly 1 (m_run may be -inf); one moving
+        // up from -inf scales the (zero) history by 0.
+        const float alpha = m_new == m_run ? 1.f : fast_exp2((m_run - m_new) * scale_log2);
+        m_run = m_new;
+        mref = m_new == neg_inf() ? 0.f : m_new * scale_log2;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+        exps();
+      }
+      l_run += ts;
     }
-    l_run += ts;
     // P^T (B operand) for the sub-block's two 16-key steps.
     bf16x8 pp[2];
 #pragma unroll
@@ -269,11 +280,21 @@ attn_fwd_short_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, co
       const char VFA_LDS* vrow = vb + S::vrow(hh * 16);
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            lds_read_tr_pair(vrow + db * 64, vrow + S::vrow(8) + db * 64), pp[hh], acc[db], 0, 0, 0);
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read_tr_pair(vrow + db * 64, vrow + S::vrow(8) + db * 64),
+                                                          pp[hh], (FIRST && hh == 0) ? f32x16{} : acc[db], 0, 0, 0);
     }
     // Sub-block j + 1 has landed (this wave's share), and nobody reads buffer j any more.
     asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
+
+  // Sub-block 0 (and Q) landed in every wave, then the workgroup barrier.
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  if (n_sub > 0) {
+    sub_block(0, std::true_type{});
+    for (int j = 1; j < n_sub; ++j) sub_block(j, std::false_type{});
+  } else {
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) acc[i] = f32x16{};
   }
 
   // Epilogue: combine the two lane halves' partial sums, normalise, store.
@@ -293,13 +314,16 @@ attn_fwd_short_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, co
       };
 #pragma unroll
       for (int gp = 0; gp < 2; ++gp) {
-        const int ga = 2 * gp, gb = 2 * gp + 1;
+        const int ga = 2 * gp, gb = 2 * gp + 1;   // the groups the lower and upper half store
         const uint32_t a0 = pk(ga * 4), a1 = pk(ga * 4 + 2), b0 = pk(gb * 4), b1 = pk(gb * 4 + 2);
+        // The swap trades lanes 32-63 of its first operand with lanes 0-31 of
+        // its second, which leaves both halves holding their 8 dims in order:
+        // a lower lane group ga (its own 4, then its partner's), an upper lane
+        // group gb (its partner's 4, then its own).
         const auto s0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
         const auto s1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
-        const u32x4 val = half == 0 ? u32x4{a0, a1, s0[1], s1[1]} : u32x4{s0[0], s1[0], b0, b1};
-        u32x4* dst = (u32x4*)(orow + db * 32 + (half == 0 ? ga : gb) * 8);
-        if (qvalid) *dst = val;
+        u32x4* dst = (u32x4*)(orow + db * 32 + (2 * gp + half) * 8);
+        if (qvalid) *dst = u32x4{s0[0], s1[0], s0[1], s1[1]};
       }
     } else {
 #pragma unroll
