@@ -64,3 +64,16 @@ def test_noalloc_prefill():
     need, out, lse, o_ref, l_ref = _both(w)
     assert need == 0
     assert torch.equal(out, o_ref) and torch.equal(lse, l_ref)
+
+
+def test_noalloc_long_prefill_counters_twice():
+    """Long-sequence prefill keeps its 1 KB of work counters in the static array: two calls in a row (the
+    second smaller, on the counters the first left behind) must each equal the workspace entry point."""
+    torch = need_gpu()
+    for name, lengths, seed in (("call 1", [1300, 513, 1029, 77, 700, 1500], 31), ("call 2", [900, 640, 33], 32)):
+        w = make_custom(lengths, num_heads_q=32, num_heads_kv=8, head_dim=128, dtype="bf16", causal=True, seed=seed)
+        assert w.total_q // w.batch >= 8 * (256 // 4)    # the persistent long-prefill kernel
+        print(f"[case] noalloc long prefill {name}: lengths {lengths}", flush=True)
+        need, out, lse, o_ref, l_ref = _both(w)
+        assert need == 1024
+        assert torch.equal(out, o_ref) and torch.equal(lse, l_ref), f"{name}: noalloc differs from varlen_attn_fwd"
