@@ -298,23 +298,29 @@ attn_fwd_short_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, co
   }
 
   // Epilogue: combine the two lane halves' partial sums, normalise, store.
-  // A lane holds, per 32-dim block and group g4, the 4 dims g4*8 + half*4 ..;
-  // for bf16 output the two halves trade one group of each pair (lane i and
-  // i + 32 own the same query), so each lane stores 8 contiguous dims (16 B).
+  // A lane holds, per 32-dim block and group g4, the 4 dims g4*8 + half*4 ..
   const float l_tot = l_run + xor_shuffle(l_run, 32);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const size_t row = (size_t)(q0 + tq) * hq + head;
-  OutT* orow = out + row * D;
+  if constexpr (sizeof(OutT) == 2) {
+    // bf16: lanes i and i + 32 (the same query) trade one group of each pair,
+    // so that each holds 8 contiguous dims (16 B); the wave lays its 32 rows
+    // out in LDS (the K/V buffers, which every wave has finished with at the
+    // last barrier) and then stores whole rows, D * 2 / 16 lanes to a row,
+    // instead of 32-byte pieces of 32 rows per store. Each row's 16-byte pad
+    // carries its output row index (-1: not stored).
+    constexpr int RS = D * 2 + 16;
+    static_assert(4 * 32 * RS <= S::TOTAL, "the four waves' rows fit in the K/V buffers");
+    char VFA_LDS* ot = (char VFA_LDS*)smem + wave * 32 * RS;
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) {
-    const f32x16& a = acc[db];
-    if constexpr (sizeof(OutT) == 2) {
+    for (int db = 0; db < D / 32; ++db) {
+      const f32x16& a = acc[db];
       auto pk = [&](int r) VFA_INLINE {
         return __builtin_bit_cast(uint32_t, f32x2_to_bf16x2(a[r] * inv, a[r + 1] * inv));
       };
 #pragma unroll
       for (int gp = 0; gp < 2; ++gp) {
-        const int ga = 2 * gp, gb = 2 * gp + 1;   // the groups the lower and upper half store
+        const int ga = 2 * gp, gb = 2 * gp + 1;   // the groups the lower and upper half keep
         const uint32_t a0 = pk(ga * 4), a1 = pk(ga * 4 + 2), b0 = pk(gb * 4), b1 = pk(gb * 4 + 2);
         // The swap trades lanes 32-63 of its first operand with lanes 0-31 of
         // its second, which leaves both halves holding their 8 dims in order:
@@ -322,10 +328,30 @@ attn_fwd_short_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, co
         // group gb (its partner's 4, then its own).
         const auto s0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
         const auto s1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
-        u32x4* dst = (u32x4*)(orow + db * 32 + (2 * gp + half) * 8);
-        if (qvalid) *dst = u32x4{s0[0], s1[0], s0[1], s1[1]};
+        *(u32x4 VFA_LDS*)(ot + l32 * RS + (db * 32 + (2 * gp + half) * 8) * 2) = u32x4{s0[0], s1[0], s0[1], s1[1]};
       }
-    } else {
+    }
+    if (half == 0) *(long long VFA_LDS*)(ot + l32 * RS + D * 2) = qvalid ? (long long)row : -1LL;
+    constexpr int LPR = D * 2 / 16;   // lanes per row
+    constexpr int RPI = 64 / LPR;     // rows per store
+    const int rsub = lane / LPR, chunk = lane % LPR;
+    // All reads first (the accumulators are dead by now), then the stores.
+    long long orow_i[32 / RPI];
+    u32x4 v[32 / RPI];
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+      const char VFA_LDS* rp = ot + (i * RPI + rsub) * RS;
+      orow_i[i] = *(const long long VFA_LDS*)(rp + D * 2);
+      v[i] = *(const u32x4 VFA_LDS*)(rp + chunk * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i)
+      if (orow_i[i] >= 0) *(u32x4*)((char*)out + orow_i[i] * (D * 2) + chunk * 16) = v[i];
+  } else {
+    OutT* orow = out + row * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const f32x16& a = acc[db];
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const f32x4 val{a[g4 * 4 + 0] * inv, a[g4 * 4 + 1] * inv, a[g4 * 4 + 2] * inv, a[g4 * 4 + 3] * inv};
