@@ -43,6 +43,14 @@
 //   O^T += V^T P^T: A = V^T read with ds_read_b64_tr_b16 (gfx950 LDS
 //                   transpose read) straight from the row-major V tile,
 //                   B = P^T converted to bf16 in registers.
+// The first sub-block has no history, so its exact max becomes the softmax
+// reference at once and its PV products start O. bf16 output leaves through
+// LDS as whole rows (16 lanes to a 256-byte row) instead of 32-byte pieces
+// of 32 rows per store.
+//
+// Batches whose key sets pass 4 GiB per sequence also come here: the
+// persistent kernel addresses a sequence through one 32-bit buffer range,
+// and this one makes a buffer per sub-block.
 #include <type_traits>
 
 #include "common.h"
