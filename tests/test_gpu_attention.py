@@ -153,6 +153,19 @@ def test_gqa_shapes(hq, hkv, d, causal):
     full_check(f"gqa Hq={hq} Hkv={hkv} D={d} causal={causal}", w)
 
 
+@pytest.mark.parametrize("batch,hq,hkv,d,out_dtype,causal", [(257, 8, 2, 64, None, True),
+                                                            (257, 8, 2, 64, None, False),
+                                                            (1000, 6, 3, 128, "fp32", True)])
+def test_many_sequences(batch, hq, hkv, d, out_dtype, causal):
+    # hundreds of short sequences: many (sequence, kv head) pairs per XCD, a pair count that is not a
+    # multiple of the 8 XCDs, and query tiles past most sequences' ends
+    lengths = np.random.default_rng(batch + d).integers(1, 160, batch)
+    w = make_custom(lengths, num_heads_q=hq, num_heads_kv=hkv, head_dim=d, dtype="bf16", causal=causal,
+                    seed=batch + hq + d)
+    assert not wide_shape(w)
+    full_check(f"many_sequences B={batch} Hq={hq} Hkv={hkv} D={d} causal={causal}", w, out_dtype=out_dtype)
+
+
 def test_unequal_lengths_bottom_right():
     # prefill-shaped with Lq != Lk (chunked prefill against a longer cache, and the reverse)
     w = make_custom([100, 7, 64, 200], [300, 7, 20, 129], num_heads_q=8, num_heads_kv=4, head_dim=128,
