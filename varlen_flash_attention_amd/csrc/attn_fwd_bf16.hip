@@ -345,16 +345,16 @@ attn_fwd_short_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, co
     const int rsub = lane / LPR, chunk = lane % LPR;
     // All reads first (the accumulators are dead by now), then the stores.
     long long orow_i[32 / RPI];
-    u32x4 v[32 / RPI];
+    u32x4 ov[32 / RPI];
 #pragma unroll
     for (int i = 0; i < 32 / RPI; ++i) {
       const char VFA_LDS* rp = ot + (i * RPI + rsub) * RS;
       orow_i[i] = *(const long long VFA_LDS*)(rp + D * 2);
-      v[i] = *(const u32x4 VFA_LDS*)(rp + chunk * 16);
+      ov[i] = *(const u32x4 VFA_LDS*)(rp + chunk * 16);
     }
 #pragma unroll
     for (int i = 0; i < 32 / RPI; ++i)
-      if (orow_i[i] >= 0) *(u32x4*)((char*)out + orow_i[i] * (D * 2) + chunk * 16) = v[i];
+      if (orow_i[i] >= 0) *(u32x4*)((char*)out + orow_i[i] * (D * 2) + chunk * 16) = ov[i];
   } else {
     OutT* orow = out + row * D;
 #pragma unroll
