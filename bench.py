@@ -455,7 +455,8 @@ def main() -> int:
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library's hot path runs on a single device "
-              "(see the sharding notes in DESIGN.md); run with --gpus 1.", file=sys.stderr)
+              "(sequences and heads would shard across GPUs, each running this path on its share); "
+              "run with --gpus 1.", file=sys.stderr)
         return 2
 
     import torch
