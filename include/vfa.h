@@ -65,7 +65,7 @@ typedef enum vfa_status {
   VFA_OK = 0,
   VFA_ERR_NULL = 1,         /* a required pointer is NULL                          */
   VFA_ERR_SHAPE = 2,        /* a size or count is out of range or inconsistent     */
-  VFA_ERR_UNSUPPORTED = 3,  /* valid request this build does not implement         */
+  VFA_ERR_UNSUPPORTED = 3,  /* valid request this library does not support         */
   VFA_ERR_WORKSPACE = 4,    /* workspace missing or smaller than the size query    */
   VFA_ERR_LAUNCH = 5        /* the HIP runtime reported an error at launch         */
 } vfa_status;

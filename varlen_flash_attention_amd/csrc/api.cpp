@@ -98,7 +98,7 @@ VFA_API const char* vfa_status_string(int32_t status) {
     case VFA_OK: return "VFA_OK: success";
     case VFA_ERR_NULL: return "VFA_ERR_NULL: a required pointer is NULL";
     case VFA_ERR_SHAPE: return "VFA_ERR_SHAPE: a size or count is out of range or inconsistent";
-    case VFA_ERR_UNSUPPORTED: return "VFA_ERR_UNSUPPORTED: request not implemented by this build";
+    case VFA_ERR_UNSUPPORTED: return "VFA_ERR_UNSUPPORTED: request not supported by this library";
     case VFA_ERR_WORKSPACE: return "VFA_ERR_WORKSPACE: workspace missing or too small";
     case VFA_ERR_LAUNCH: return "VFA_ERR_LAUNCH: the HIP runtime reported a launch error";
     default: return "unknown vfa status";
