@@ -19,13 +19,18 @@ pytestmark = pytest.mark.gpu
 def test_graph_capture_and_replay(monkeypatch):
     torch = need_gpu()
     monkeypatch.delenv("VFA_DEBUG", raising=False)          # the debug check synchronises: not capturable
-    print("[case] graph capture of prefill, decode, merge, paged decode, prologue and gated delta rule", flush=True)
+    print("[case] graph capture of short and long prefill, decode, merge, paged decode, prologue and gated delta rule",
+          flush=True)
     wp = make_custom([300, 77, 513], num_heads_q=32, num_heads_kv=8, head_dim=128, dtype="bf16", causal=True, seed=120)
+    # long-sequence prefill: the persistent kernel, whose work counters a kernel (not a memset) clears per call
+    wl = make_custom([1300, 513, 1029, 77, 700, 1500], num_heads_q=32, num_heads_kv=8, head_dim=128, dtype="bf16",
+                     causal=True, seed=125)
+    assert wl.total_q // wl.batch >= 8 * (256 // 4)
     wd = make_custom([1] * 4, [5000, 300, 9000, 70], num_heads_q=32, num_heads_kv=4, head_dim=128, dtype="bf16",
                      causal=True, seed=121)
     pc = make_paged(wd, 16, seed=12)
     pro = make_prologue([50, 300], 32, 8, 128, seed=122)
-    dp, dd = to_device(wp), to_device(wd)
+    dp, dd, dl = to_device(wp), to_device(wd), to_device(wl)
     kc, vc = dev_array(pc.k_cache, "bf16"), dev_array(pc.v_cache, "bf16")
     table, used = torch.from_numpy(pc.block_table).cuda(), torch.from_numpy(pc.seqused_k).cuda()
     rng = np.random.default_rng(123)
@@ -49,6 +54,8 @@ def test_graph_capture_and_replay(monkeypatch):
                                  softmax_scale=wp.scale, causal=True),
             *vfa.varlen_attn_fwd(dd["q"], dd["k"], dd["v"], dd["cu_q"], dd["cu_k"], wd.max_seqlen_q, wd.max_seqlen_k,
                                  softmax_scale=wd.scale, causal=True),
+            *vfa.varlen_attn_fwd(dl["q"], dl["k"], dl["v"], dl["cu_q"], dl["cu_k"], wl.max_seqlen_q, wl.max_seqlen_k,
+                                 softmax_scale=wl.scale, causal=True),
             *vfa.attn_update(lse_p, go, update_type=1),
             *vfa.paged_attn_decode(dd["q"], kc, vc, table, dd["cu_q"], used, wd.max_seqlen_q, wd.max_seqlen_k,
                                    softmax_scale=wd.scale, causal=True),
