@@ -77,3 +77,49 @@ def test_noalloc_long_prefill_counters_twice():
         need, out, lse, o_ref, l_ref = _both(w)
         assert need == 1024
         assert torch.equal(out, o_ref) and torch.equal(lse, l_ref), f"{name}: noalloc differs from varlen_attn_fwd"
+
+
+def test_noalloc_under_graph_capture():
+    """The callers this entry point is for: a decode call (partials in the static array) and a long-prefill call
+    (work counters in it) captured into one HIP graph; three replays, with eager work on the outputs and elsewhere
+    between them, each equal the eager result bit for bit."""
+    torch = need_gpu()
+    print("[case] noalloc under graph capture: decode workload and long prefill", flush=True)
+    wd = make_workload("decode")
+    wl = make_custom([1300, 513, 1029, 77, 700, 1500], num_heads_q=32, num_heads_kv=8, head_dim=128, dtype="bf16",
+                     causal=True, seed=33)
+    calls = []
+    for w in (wd, wl):
+        d = to_device(w)
+        out = torch.empty((w.total_q, w.num_heads_q, w.head_dim), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((w.total_q, w.num_heads_q), dtype=torch.float32, device="cuda")
+        calls.append((w, d, out, lse))
+
+    def run_all():
+        for w, d, out, lse in calls:
+            vfa.varlen_attn_fwd_noalloc(d["q"], d["k"], d["v"], d["cu_q"], d["cu_k"], w.max_seqlen_q,
+                                        w.max_seqlen_k, out, lse, softmax_scale=w.scale, causal=w.causal)
+
+    run_all()
+    torch.cuda.synchronize()
+    ref = [(out.clone(), lse.clone()) for _, _, out, lse in calls]
+    side = torch.cuda.Stream()                                 # default priority
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run_all()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run_all()
+    for rep in range(3):
+        for _, _, out, lse in calls:
+            out.zero_()
+            lse.zero_()
+        junk = torch.randn(1 << 20, device="cuda").sum()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert float(junk) == float(junk)
+        for i, ((_, _, out, lse), (o_ref, l_ref)) in enumerate(zip(calls, ref)):
+            assert torch.equal(out, o_ref) and torch.equal(lse, l_ref), f"replay {rep}: call {i} differs"
