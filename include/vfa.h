@@ -7,8 +7,8 @@
  *     that the caller allocates, owns and frees. The library never allocates,
  *     frees, synchronises or copies device memory to the host, and keeps no
  *     state between calls (it is reentrant). The one exception is
- *     varlen_attn_fwd_noalloc, whose split-KV partials live in a static
- *     per-device array (see there).
+ *     varlen_attn_fwd_noalloc, whose split-KV partials and long-prefill work
+ *     counters live in a static per-device array (see there).
  *   - `stream` is a hipStream_t (NULL = the null stream). Work is enqueued
  *     on it asynchronously; results are ready when the stream reaches them.
  *   - Sizes and flags are HOST values. Every condition that can be checked
@@ -182,8 +182,10 @@ int32_t varlen_attn_fwd_offset(const void* q, const void* k, const void* v, int3
 
 /* varlen_attn_fwd for callers that cannot allocate device memory: code
  * under HIP graph capture, tight serving loops, harnesses that forbid
- * hipMalloc. It takes no workspace: the split-KV partials go to a static
- * device array of VFA_STATIC_SCRATCH_BYTES (16 MiB) that every device the
+ * hipMalloc. It takes no workspace: the split-KV partials, and the 1 KB of
+ * work counters of long-sequence prefill (cleared by a kernel on every
+ * call), go to a static device array of VFA_STATIC_SCRATCH_BYTES (16 MiB)
+ * that every device the
  * library runs on holds from the moment the library's code is loaded there
  * until the process ends. The call itself allocates and frees nothing and
  * calls no allocating library routine; the first call on a device looks up
