@@ -185,9 +185,8 @@ int32_t varlen_attn_fwd_offset(const void* q, const void* k, const void* v, int3
  * hipMalloc. It takes no workspace: the split-KV partials, and the 1 KB of
  * work counters of long-sequence prefill (cleared by a kernel on every
  * call), go to a static device array of VFA_STATIC_SCRATCH_BYTES (16 MiB)
- * that every device the
- * library runs on holds from the moment the library's code is loaded there
- * until the process ends. The call itself allocates and frees nothing and
+ * that every device the library runs on holds from the moment the library's
+ * code is loaded there until the process ends. The call itself allocates and frees nothing and
  * calls no allocating library routine; the first call on a device looks up
  * that device's copy of the array (hipGetSymbolAddress) and caches it.
  *
