@@ -9,7 +9,7 @@ import pytest
 
 import oracle
 import varlen_flash_attention_amd as vfa
-from varlen_flash_attention_amd.workloads import make_custom, make_workload
+from varlen_flash_attention_amd.workloads import make_custom, make_growing_scores, make_workload
 from tests.gpu_util import check, host64, need_gpu, tile_tokens, to_device
 
 pytestmark = pytest.mark.gpu
@@ -164,6 +164,24 @@ def test_many_sequences(batch, hq, hkv, d, out_dtype, causal):
                     seed=batch + hq + d)
     assert not wide_shape(w)
     full_check(f"many_sequences B={batch} Hq={hq} Hkv={hkv} D={d} causal={causal}", w, out_dtype=out_dtype)
+
+
+@pytest.mark.parametrize("lengths,hq,hkv,dtype,causal,wide", [
+    ([200, 513, 37, 300], 8, 2, "bf16", True, False),
+    ([200, 513, 37, 300], 8, 2, "bf16", False, False),
+    ([1300, 513, 1029, 700, 1500], 32, 8, "bf16", True, True),
+    ([1300, 513, 1029, 700, 1500], 32, 8, "bf16", False, True),
+])
+def test_growing_scores_move_the_reference(lengths, hq, hkv, dtype, causal, wide):
+    # Scores that climb by about 8 log2 units per 32 keys: the bf16 kernels' running sum against their lazy
+    # softmax reference passes 2^32 every few sub-blocks, so the rescale path runs many times per row (both
+    # the short-sequence and the long-sequence kernel). The fp32 kernel has no lazy reference (it rescales
+    # whenever the max grows) and is not run here: at raw scores near 1000, fp32 rounding of q . k alone
+    # moves lse by about two fp32 ulps of its value (~88), past the fp32 tolerance of 1e-5.
+    w = make_growing_scores(lengths, num_heads_q=hq, num_heads_kv=hkv, head_dim=128, dtype=dtype, causal=causal,
+                            seed=sum(lengths) + hq)
+    assert wide_shape(w) == wide
+    full_check(f"growing_scores {dtype} Hq={hq} causal={causal} wide={wide}", w)
 
 
 def test_unequal_lengths_bottom_right():

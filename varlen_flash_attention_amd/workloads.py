@@ -32,6 +32,7 @@ import numpy as np
 
 __all__ = [
     "Workload",
+    "make_growing_scores",
     "round_to_bf16",
     "bf16_bits",
     "make_workload",
@@ -260,6 +261,32 @@ def make_custom(lengths_q, lengths_k=None, num_heads_q=4, num_heads_kv=2, head_d
     return Workload(name=name, lengths_q=lq, lengths_k=lk, num_heads_q=num_heads_q,
                     num_heads_kv=num_heads_kv, head_dim=head_dim, dtype=dtype,
                     causal=bool(causal), scale=sc, seed=seed, q=q, k=k, v=v)
+
+
+def make_growing_scores(lengths, num_heads_q=8, num_heads_kv=2, head_dim=128, dtype="bf16", causal=True,
+                        seed=0, top_score=1000.0, name="growing_scores") -> Workload:
+    """Scores that climb along every sequence: Q entries near 1 and key row j of a sequence of length L
+    scaled by (j + 1) / L, so q . k runs from about 0 to about ``top_score`` (raw, before the softmax scale)
+    over each sequence, with noise of a tenth around the trend. With the default scale 1/sqrt(D) a row's
+    later keys then outgrow its earlier ones by far more than 2^32 in probability units, which moves an
+    online softmax's reference several times per row."""
+    lq = np.asarray(lengths, dtype=np.int64).reshape(-1)
+    sq, sk, sv = np.random.SeedSequence(seed).spawn(3)
+    tq = int(lq.sum())
+    q = 1.0 + 0.1 * _normal(sq, (tq, num_heads_q, head_dim))
+    k = 1.0 + 0.1 * _normal(sk, (tq, num_heads_kv, head_dim))
+    v = _normal(sv, (tq, num_heads_kv, head_dim))
+    ramp = np.concatenate([(np.arange(n, dtype=np.float64) + 1.0) / max(int(n), 1) for n in lq]) if tq else \
+        np.zeros(0)
+    k = k * (top_score / head_dim * ramp)[:, None, None]
+    q, k, v = (np.ascontiguousarray(t, dtype=np.float32) for t in (q, k, v))
+    if dtype == "bf16":
+        q, k, v = (round_to_bf16(t, inplace=True) for t in (q, k, v))
+    elif dtype != "fp32":
+        raise ValueError(f"unknown dtype {dtype!r}")
+    return Workload(name=name, lengths_q=lq, lengths_k=lq.copy(), num_heads_q=num_heads_q,
+                    num_heads_kv=num_heads_kv, head_dim=head_dim, dtype=dtype, causal=bool(causal),
+                    scale=1.0 / math.sqrt(head_dim), seed=seed, q=q, k=k, v=v)
 
 
 def chunk_bounds(length: int, sp: int) -> list[tuple[int, int]]:
