@@ -11,8 +11,8 @@ import sys
 import numpy as np
 import pytest
 
-from varlen_flash_attention_amd.workloads import (bf16_bits, chunk_bounds, make_custom, make_workload,
-                                                  round_to_bf16)
+from varlen_flash_attention_amd.workloads import (bf16_bits, chunk_bounds, make_custom, make_growing_scores,
+                                                  make_workload, round_to_bf16)
 
 REPO = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -85,6 +85,20 @@ def test_values_are_seeded_and_bf16_exact():
 
 
 # ------------------------------------------------------------------ bf16 rounding
+
+def test_growing_scores_workload():
+    # seeded, bf16-exact, and the documented climb: a row's raw scores run from about 0 to about top_score
+    a = make_growing_scores([300, 5], num_heads_q=4, num_heads_kv=2, head_dim=64, dtype="bf16", seed=3,
+                            top_score=800.0)
+    b = make_growing_scores([300, 5], num_heads_q=4, num_heads_kv=2, head_dim=64, dtype="bf16", seed=3,
+                            top_score=800.0)
+    assert all(np.array_equal(x, y) for x, y in ((a.q, b.q), (a.k, b.k), (a.v, b.v)))
+    bf16_bits(a.q), bf16_bits(a.k), bf16_bits(a.v)           # raises unless bf16-exact
+    s = a.q[299, 0].astype(np.float64) @ a.k[:300, 0].astype(np.float64).T
+    assert 0 < s[0] < 20 and 700 < s[-1] < 900
+    assert np.all(np.diff(s[::30]) > 0)                      # climbs along the sequence
+    assert a.lengths_q.tolist() == a.lengths_k.tolist() == [300, 5]
+
 
 def test_round_to_bf16_ties_to_even_and_bits():
     one = 1.0
