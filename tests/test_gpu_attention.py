@@ -184,6 +184,17 @@ def test_growing_scores_move_the_reference(lengths, hq, hkv, dtype, causal, wide
     full_check(f"growing_scores {dtype} Hq={hq} causal={causal} wide={wide}", w)
 
 
+@pytest.mark.parametrize("causal", [True, False])
+def test_long_prefill_unequal_and_empty_keys(causal):
+    # the persistent long-sequence kernel through the plain entry point with Lk < Lq (bottom-right causal
+    # alignment leaves the first Lq - Lk rows without a visible key), Lk > Lq and empty key sets
+    lq = [1300, 513, 1029, 77, 700, 1500]
+    lk = [900, 513, 0, 300, 1400, 40]
+    w = make_custom(lq, lk, num_heads_q=32, num_heads_kv=8, head_dim=128, dtype="bf16", causal=causal, seed=126)
+    assert wide_shape(w)
+    full_check(f"long_prefill_unequal causal={causal}", w)
+
+
 def test_unequal_lengths_bottom_right():
     # prefill-shaped with Lq != Lk (chunked prefill against a longer cache, and the reverse)
     w = make_custom([100, 7, 64, 200], [300, 7, 20, 129], num_heads_q=8, num_heads_kv=4, head_dim=128,
