@@ -185,6 +185,15 @@ def test_growing_scores_move_the_reference(lengths, hq, hkv, dtype, causal, wide
 
 
 @pytest.mark.parametrize("causal", [True, False])
+def test_long_prefill_head_dim_64(causal):
+    # the persistent long-sequence kernel's D = 64 instance, with ragged tails
+    w = make_custom([1100, 600, 901, 33], num_heads_q=16, num_heads_kv=4, head_dim=64, dtype="bf16",
+                    causal=causal, seed=127)
+    assert wide_shape(w)
+    full_check(f"long_prefill_d64 causal={causal}", w)
+
+
+@pytest.mark.parametrize("causal", [True, False])
 def test_long_prefill_unequal_and_empty_keys(causal):
     # the persistent long-sequence kernel through the plain entry point with Lk < Lq (bottom-right causal
     # alignment leaves the first Lq - Lk rows without a visible key), Lk > Lq and empty key sets
