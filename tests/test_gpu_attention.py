@@ -184,6 +184,17 @@ def test_growing_scores_move_the_reference(lengths, hq, hkv, dtype, causal, wide
     full_check(f"growing_scores {dtype} Hq={hq} causal={causal} wide={wide}", w)
 
 
+@pytest.mark.parametrize("lengths,hq,hkv", [([2500, 3000, 900], 4, 4),      # G = 1: 256-token tiles
+                                             ([900, 700, 503], 12, 4),       # G = 3: 85 tokens, one column idle
+                                             ([300, 150, 77], 32, 2)])       # G = 16: 16-token tiles
+@pytest.mark.parametrize("causal", [True, False])
+def test_long_prefill_group_sizes(lengths, hq, hkv, causal):
+    w = make_custom(lengths, num_heads_q=hq, num_heads_kv=hkv, head_dim=128, dtype="bf16", causal=causal,
+                    seed=128 + hq)
+    assert wide_shape(w)
+    full_check(f"long_prefill G={hq // hkv} causal={causal}", w)
+
+
 @pytest.mark.parametrize("causal", [True, False])
 def test_long_prefill_head_dim_64(causal):
     # the persistent long-sequence kernel's D = 64 instance, with ragged tails
