@@ -222,13 +222,15 @@ def test_unequal_lengths_bottom_right():
     full_check("unequal_lengths causal", w)
 
 
-def test_bf16_in_fp32_out():
-    w = make_custom([77, 256, 3], num_heads_q=8, num_heads_kv=2, head_dim=128, dtype="bf16", causal=True, seed=80)
-    print("[case] bf16 in, fp32 out", flush=True)
+@pytest.mark.parametrize("lengths,wide", [([77, 256, 3], False), ([1300, 513, 1029, 70], True)])
+def test_bf16_in_fp32_out(lengths, wide):
+    w = make_custom(lengths, num_heads_q=8, num_heads_kv=2, head_dim=128, dtype="bf16", causal=True, seed=80)
+    assert wide_shape(w) == wide
+    print(f"[case] bf16 in, fp32 out, wide={wide}", flush=True)
     out, lse = run_gpu(w, out_dtype="fp32")
     assert str(out.dtype) == "torch.float32"
     o_ref, l_ref = run_oracle(w)
-    check("bf16_in_fp32_out", host64(out), host64(lse), o_ref, l_ref, "bf16")
+    check(f"bf16_in_fp32_out wide={wide}", host64(out), host64(lse), o_ref, l_ref, "bf16")
 
 
 @pytest.mark.parametrize("hq,hkv,lq,d,causal", [
