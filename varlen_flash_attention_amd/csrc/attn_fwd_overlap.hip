@@ -26,15 +26,14 @@
 // caller's workspace and a one-wave kernel zeroes them before each call.
 //
 // Software pipeline. Per 32-key sub-block a wave runs S_j^T = K_j Q^T (8
-// MFMAs), the online softmax of S_j (exponentials on the transcendental unit,
-// sums and conversions on the VALU) and O^T += V_j^T P_j^T (8 MFMAs). PV_j
+// MFMAs), the online softmax of S_j (exponentials, sums and bf16 conversions
+// on the vector ALU) and O^T += V_j^T P_j^T (8 MFMAs). PV_j
 // needs the softmax of S_j, and the softmax needs QK_j, so a wave that runs
 // them in that order leaves the matrix unit idle during its softmax. Here
 // iteration j issues QK_{j+1} and PV_{j-1}, which need nothing from iteration
 // j, and the softmax of S_j between those 16 MFMAs, in a pinned instruction
-// order, so the transcendental and vector units work under the MFMAs of the
-// same wave. The two waves of each SIMD run this freely and fill each other's
-// remaining gaps.
+// order, so the vector ALU works under the MFMAs of the same wave. The two
+// waves of each SIMD run this freely and fill each other's remaining gaps.
 //
 // K and V stream through LDS rings of 4 sub-block slots with one barrier per
 // tile of 2 sub-blocks. Waves 0-3 move K and waves 4-7 move V, one sub-block
@@ -62,7 +61,7 @@ constexpr int kSub = 32;        // keys per sub-block
 constexpr int kRing = 4;        // sub-block slots per LDS ring (two tiles of two)
 constexpr int kTicketStride = 32;   // ints between two XCDs' counters (one 128-byte line each)
 
-// LDS row strides as in the general kernel: a 16-byte pad keeps the
+// LDS row strides as in the short-sequence kernel: a 16-byte pad keeps the
 // per-lane-row ds_read_b128 of K conflict-free, a 64-byte pad the transposed
 // reads of V.
 template <int D>
@@ -307,8 +306,7 @@ attn_fwd_overlap_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, 
   // One iteration: the softmax of sub-block j (scores in s_cur, P_j into
   // p_cur) between the MFMAs of QK_{j+1} (into s_next) and PV_{j-1} (with
   // p_prev), plus the group's staging. A reference move (the slow path)
-  // recomputes P_j. `st` is the staging set that holds
-  // sub-block j + ahead.
+  // recomputes P_j. `st` is the staging set that holds sub-block j + ahead.
   auto step = [&](auto do_qk, auto do_pv, int j, f32x16& s_cur, f32x16& s_next, bf16x8 (&p_cur)[2],
                   const bf16x8 (&p_prev)[2], u32x4 (&st)[PT]) VFA_INLINE {
     constexpr bool QK = decltype(do_qk)::value, PV = decltype(do_pv)::value;
@@ -432,8 +430,9 @@ attn_fwd_overlap_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k, 
   using no = std::integral_constant<bool, false>;
   f32x16 sa, sb;
   bf16x8 pa[2], pb[2];
-  // Iteration j uses scores / probabilities a or b by the parity of j. A tile barrier precedes every even iteration after the
-  // first, and the final PV when it falls on an even position.
+  // Iteration j uses scores / probabilities a or b by the parity of j. A tile
+  // barrier precedes every even iteration after the first, and the final PV
+  // when it falls on an even position.
   if (n_sub > 0) {
     // QK_0 reads K_0, whose slot iteration 1 refills with K_4: every wave's
     // reads of it complete before any wave goes on.
