@@ -22,9 +22,9 @@ typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// 2^x on the transcendental unit. -inf -> 0.
+// 2^x by the hardware instruction (v_exp_f32). -inf -> 0.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-// log2(x) on the transcendental unit (x > 0).
+// log2(x) by the hardware instruction (v_log_f32), x > 0.
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
