@@ -28,7 +28,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kLanesPerCol = 8;         // lanes sharing one state column
 constexpr int kColsPerBlock = kThreads / kLanesPerCol;   // 32 state columns per workgroup
-constexpr int kTC = 16;                 // tokens staged per round (the calls this kernel serves fit one)
+constexpr int kTC = 16;                 // tokens staged per pass (the calls this kernel serves fit one)
 
 // Sum over 8 consecutive lanes with DPP: within each quad (lane ^ 1, then
 // lane ^ 2), then across the two quads of the 8 (row_half_mirror pairs lane i
@@ -103,7 +103,7 @@ __global__ __launch_bounds__(kThreads) void gated_delta_kernel(
 
   for (int c0 = 0; c0 < len; c0 += kTC) {
     const int n = min(kTC, len - c0);
-    __syncthreads();                     // previous round's reads are done
+    __syncthreads();                     // the previous staging pass is no longer read
     // Stage q and k rows (bf16 -> fp32), this block's v columns, g and beta.
     for (int e = tid; e < kTC * (DK / 2); e += kThreads) {
       const int t = e / (DK / 2), d2 = (e % (DK / 2)) * 2;
