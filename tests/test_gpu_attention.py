@@ -185,8 +185,12 @@ def test_growing_scores_move_the_reference(lengths, hq, hkv, dtype, causal, wide
 
 
 @pytest.mark.parametrize("lengths,hq,hkv", [([2500, 3000, 900], 4, 4),      # G = 1: 256-token tiles
+                                             ([1500, 1200, 700], 4, 2),      # G = 2: 128-token tiles
                                              ([900, 700, 503], 12, 4),       # G = 3: 85 tokens, one column idle
-                                             ([300, 150, 77], 32, 2)])       # G = 16: 16-token tiles
+                                             ([700, 400, 333], 12, 2),       # G = 6: 42 tokens, four columns idle
+                                             ([600, 333, 290], 16, 2),       # G = 8: 32 tokens, a head per wave
+                                             ([300, 150, 77], 32, 2),        # G = 16: 16-token tiles
+                                             ([150, 97, 40], 32, 1)])        # G = 32: 8 tokens, four heads per wave
 @pytest.mark.parametrize("causal", [True, False])
 def test_long_prefill_group_sizes(lengths, hq, hkv, causal):
     w = make_custom(lengths, num_heads_q=hq, num_heads_kv=hkv, head_dim=128, dtype="bf16", causal=causal,
