@@ -108,3 +108,27 @@ def test_random_shape(i):
     o_ref, l_ref = oracle.varlen_attention(w.q, w.k, w.v, w.cu_seqlens_q, w.cu_seqlens_k, w.num_heads_kv, w.scale,
                                            w.causal)
     check(name, host64(out), host64(lse), o_ref, l_ref, w.dtype)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("i", range(0, N_CASES, 2))
+def test_random_shape_causal_offset(i):
+    # the same shapes through the explicit-alignment entry point, causal, with per-sequence offsets of every
+    # kind (bottom-right, top-left, chunk-style negative, past every key, below every row, random)
+    from tests.test_gpu_causal_offset import offsets_for
+    torch = need_gpu()
+    p = draw_case(i)
+    offs = offsets_for(p["lq"].tolist(), p["lk"].tolist(), np.random.default_rng(p["seed"] + 5))
+    name = (f"random offset case {i}: seed={p['seed']} route={route(p)} Lq={p['lq'].tolist()} Lk={p['lk'].tolist()} "
+            f"offsets={offs} Hq={p['hq']} Hkv={p['hkv']} D={p['d']} {p['dtype']}")
+    print(f"[case] {name}", flush=True)
+    w = make_custom(p["lq"], p["lk"], num_heads_q=p["hq"], num_heads_kv=p["hkv"], head_dim=p["d"], dtype=p["dtype"],
+                    causal=True, seed=p["seed"], name=f"random_offset{i}")
+    dv = to_device(w)
+    off = torch.tensor(np.asarray(offs, dtype=np.int32), device="cuda")
+    out, lse = vfa.varlen_attn_fwd(dv["q"], dv["k"], dv["v"], dv["cu_q"], dv["cu_k"], w.max_seqlen_q, w.max_seqlen_k,
+                                   softmax_scale=w.scale, causal=True, causal_offset=off)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.varlen_attention(w.q, w.k, w.v, w.cu_seqlens_q, w.cu_seqlens_k, w.num_heads_kv, w.scale,
+                                           True, causal_offset=offs)
+    check(name, host64(out), host64(lse), o_ref, l_ref, w.dtype)
