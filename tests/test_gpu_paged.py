@@ -160,3 +160,31 @@ def test_paged_debug_check(monkeypatch):
         run_paged(w, pc, d={**d, "used": bad_used})
     assert e.value.status == 2
     monkeypatch.delenv("VFA_DEBUG")
+
+
+def draw_paged_case(i):
+    """Seeded random paged-decode shape: batch 1-8, 1-7 query tokens per sequence, 0-6000 keys, pages of
+    16-256 keys (powers of two), Hkv 1-8 with G 1-8, D 64 or 128, either mask, bf16 or fp32 output."""
+    rng = np.random.default_rng(6100 + i)
+    b = int(rng.integers(1, 9))
+    lq = rng.integers(1, 8, b) if rng.random() < 0.3 else np.ones(b, dtype=np.int64)
+    lk = rng.integers(0, 6001, b)
+    lk[rng.random(b) < 0.15] = 0
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    g = int(rng.choice([1, 2, 3, 4, 8]))
+    return dict(page=int(rng.choice([16, 32, 64, 128, 256])), lq=[int(x) for x in lq], lk=[int(x) for x in lk],
+                hq=hkv * g, hkv=hkv, d=int(rng.choice([64, 128])), causal=bool(rng.integers(2)),
+                out_dtype="fp32" if rng.random() < 0.25 else None, seed=6200 + i)
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_paged_random_shape(i):
+    need_gpu()
+    c = draw_paged_case(i)
+    w = make_custom(c["lq"], c["lk"], num_heads_q=c["hq"], num_heads_kv=c["hkv"], head_dim=c["d"], dtype="bf16",
+                    causal=c["causal"], seed=c["seed"])
+    pc = make_paged(w, c["page"], seed=c["seed"] + 1)
+    describe(f"paged random case {i} (seed {c['seed']}, out {c['out_dtype'] or 'bf16'})", w, pc)
+    out, lse = run_paged(w, pc, out_dtype=c["out_dtype"])
+    o_ref, l_ref = run_oracle(w, pc)
+    check(f"paged random case {i}", host64(out), host64(lse), o_ref, l_ref, "bf16")
